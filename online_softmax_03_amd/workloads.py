@@ -1,0 +1,120 @@
+"""Seeded synthetic workloads for the attention forward.
+
+This module only draws inputs: it holds the workload table (shapes, dtypes,
+value distributions, masks, seeds) and a generator. It contains none of the
+attention arithmetic, so both the HIP path's tests and the CPU oracle can take
+their inputs from here without sharing any computation.
+
+Every tensor is drawn in float32 from a CPU ``torch.Generator`` seeded per
+workload, in the order Q, K, V (then the key lengths), and only then rounded
+to the workload's input dtype (round-to-nearest-even). The rounded values are
+what both sides receive.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    in_dtype: str            # "f32" | "bf16" | "f16"
+    out_dtype: str           # dtype of O; LSE is always float32
+    causal: bool
+    q_dist: tuple            # ("normal", sd) or ("uniform", lo, hi)
+    k_dist: tuple
+    v_dist: tuple
+    key_padding: bool = False   # per-batch valid key length ~ U{0..N}
+    block_c: Optional[int] = None  # forced key-tile width, None = library default
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d) rounded to float32: the value the library receives."""
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32))
+
+    def nominal_flops(self) -> float:
+        """4*B*H*N^2*d multiply-adds-as-two-flops, halved for a causal mask."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def with_shape(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the attention forward study, in order. Index 0 is the
+# small case the oracle finishes in seconds; index 2 is the headline case.
+WORKLOADS = [
+    Workload("tiny_f32_n256_d64", 1, 1, 256, 64, "f32", "f32", False,
+             ("normal", 1.0), ("normal", 1.0), ("normal", 1.0), block_c=64, seed=1000),
+    Workload("bf16_noncausal_n2048_d64", 4, 16, 2048, 64, "bf16", "f32", False,
+             ("normal", 1.0), ("normal", 1.0), ("normal", 1.0), seed=1001),
+    Workload("bf16_causal_n8192_d128", 2, 32, 8192, 128, "bf16", "bf16", True,
+             ("normal", 1.0), ("normal", 1.0), ("normal", 1.0), seed=1002),
+    # Q variance 4 (sd 2): large logits, so the running max moves often.
+    Workload("bf16_causal_long_n32768_d128", 1, 8, 32768, 128, "bf16", "bf16", True,
+             ("normal", 2.0), ("normal", 1.0), ("normal", 1.0), seed=1003),
+    Workload("f16_keypad_n4096_d64", 8, 16, 4096, 64, "f16", "f16", False,
+             ("normal", 3.0), ("normal", 3.0), ("uniform", -1.0, 1.0),
+             key_padding=True, seed=1004),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def _draw(gen: torch.Generator, shape, dist) -> torch.Tensor:
+    if dist[0] == "normal":
+        return torch.randn(shape, generator=gen, dtype=torch.float32) * dist[1]
+    if dist[0] == "uniform":
+        lo, hi = dist[1], dist[2]
+        return torch.rand(shape, generator=gen, dtype=torch.float32) * (hi - lo) + lo
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def key_lengths(gen: torch.Generator, B: int, N: int) -> torch.Tensor:
+    """Per-batch valid key length drawn uniformly from {0..N}; the first batch
+    is forced to 0 (every row fully masked) and the last to N (no padding) so
+    both extremes are always present."""
+    lens = torch.randint(0, N + 1, (B,), generator=gen, dtype=torch.int64)
+    lens[0] = 0
+    if B > 1:
+        lens[B - 1] = N
+    return lens
+
+
+def mask_from_lengths(lens: torch.Tensor, N: int) -> torch.Tensor:
+    """[B][N] uint8, 1 where the key is valid (j < len_b), 0 where padded."""
+    j = torch.arange(N, dtype=torch.int64)
+    return (j[None, :] < lens[:, None]).to(torch.uint8).contiguous()
+
+
+def generate(w: Workload, seed: Optional[int] = None, lens: Optional[torch.Tensor] = None) -> dict:
+    """Draw Q, K, V ([B][H][N][d], contiguous, CPU) and the key mask.
+
+    Returns a dict with q, k, v (in_dtype), mask (uint8 [B][N] or None),
+    lens (int64 [B] or None), scale (float32 value as a Python float), causal,
+    in_dtype / out_dtype names.
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.N, w.d)
+    dt = DTYPES[w.in_dtype]
+    q = _draw(gen, shape, w.q_dist).to(dt).contiguous()
+    k = _draw(gen, shape, w.k_dist).to(dt).contiguous()
+    v = _draw(gen, shape, w.v_dist).to(dt).contiguous()
+    mask = None
+    if w.key_padding or lens is not None:
+        if lens is None:
+            lens = key_lengths(gen, w.B, w.N)
+        mask = mask_from_lengths(lens, w.N)
+    return dict(q=q, k=k, v=v, mask=mask, lens=lens, scale=w.scale, causal=w.causal,
+                in_dtype=w.in_dtype, out_dtype=w.out_dtype, workload=w)

@@ -1,0 +1,13 @@
+"""CPU oracle for the attention forward with online softmax.
+
+TEST INFRASTRUCTURE ONLY. The tests, the smoke check and the benchmark's CPU
+baseline import this package; the product path (the HIP library and its
+Python binding) never does, and the two share no code.
+
+- `attention(...)`: float64 three-pass safe-softmax attention (plain C).
+- `softmax_ref.safe_softmax`, `softmax_ref.online_softmax`,
+  `softmax_ref.online_attention`, `softmax_ref.merge_states`: score-level and
+  blocked references used to pin the three-pass oracle (and vice versa).
+"""
+from .attention import attention, build, load, max_threads  # noqa: F401
+from . import softmax_ref  # noqa: F401

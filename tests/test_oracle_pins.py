@@ -1,0 +1,416 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these checks compares the oracle with itself: they use the numbers
+the pages print for their worked examples, closed forms, a different formula
+(the naive exp/sum softmax, valid at small magnitudes), a library routine
+(torch's float64 scaled-dot-product attention), a different algorithm (the
+blocked online recurrence, for every block size), invariants and special
+cases with known answers.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import softmax_ref as sr
+from online_softmax_03_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+E = math.exp
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _example(ident):
+    for ex in _golden()["examples"]:
+        if ex["id"] == ident:
+            return ex
+    raise KeyError(ident)
+
+
+def _rand(shape, seed, sd=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g, dtype=torch.float64) * sd).numpy()
+
+
+# ----------------------------------------------------------------------------
+# printed worked examples (score-level)
+# ----------------------------------------------------------------------------
+
+def test_example_blocks_2_4_then_1_3():
+    ex = _example("blocks_2_4_then_1_3")
+    tol = ex["tol"]
+    r = sr.online_softmax(ex["blocks"])
+    t0, t1 = r["trace"]
+    assert t0["m_cand"] == ex["printed"]["after_block_0"]["m"]
+    assert abs(t0["l_after"] - ex["printed"]["after_block_0"]["l"]) <= tol
+    # block 1's maximum (3) is below m (4): the rescale factor is exactly 1
+    assert t1["alpha"] == 1.0
+    assert np.allclose(t1["P"], ex["printed"]["block_1_terms"], atol=tol, rtol=0)
+    assert r["m"] == ex["printed"]["final"]["m"]
+    assert abs(r["l"] - ex["printed"]["final"]["l"]) <= tol
+    exact = E(2 - 4) + E(0) + E(1 - 4) + E(3 - 4)
+    assert abs(r["l"] - exact) <= 1e-14
+    _, m, l, lse = sr.safe_softmax(sum(ex["blocks"], []))
+    assert m == 4 and abs(l - exact) <= 1e-14 and abs(lse - (4 + math.log(exact))) <= 1e-14
+
+
+def test_example_blocks_1_2_then_5_3():
+    ex = _example("blocks_1_2_then_5_3")
+    pr, tol = ex["printed"], ex["tol"]
+    r = sr.online_softmax(ex["blocks"])
+    t0, t1 = r["trace"]
+    assert t0["m_cand"] == pr["after_block_0"]["m"]
+    # starting from m = -inf the first rescale factor is exp(-inf) = 0
+    assert t0["alpha"] == pr["after_block_0"]["alpha"]
+    assert abs(t0["l_after"] - pr["after_block_0"]["l"]) <= tol
+    assert t1["m_cand"] == pr["block_1"]["m_cand"]
+    assert abs(t1["alpha"] - pr["block_1"]["alpha"]) <= tol
+    assert abs(t1["l_scaled"] - pr["block_1"]["l_scaled"]) <= tol
+    assert np.allclose(t1["P"], pr["block_1"]["terms"], atol=tol, rtol=0)
+    assert r["m"] == pr["final"]["m"]
+    assert abs(r["l"] - pr["final"]["l"]) <= tol
+    assert abs(r["l"] - pr["check_sum"]) <= ex["tol_check_sum"]
+    exact = E(1 - 5) + E(2 - 5) + E(0) + E(3 - 5)
+    assert abs(r["l"] - exact) <= 1e-14
+    assert abs(t1["alpha"] - E(-3)) <= 1e-16
+
+
+def test_example_chunks_1_2_then_3_10_with_unit_values():
+    ex = _example("chunks_1_2_then_3_10_v_ones")
+    pr, tol = ex["printed"], ex["tol"]
+    v = np.asarray(ex["v"], dtype=np.float64)[:, None]
+    r = sr.online_softmax(ex["blocks"], [v[:2], v[2:]])
+    t0, t1 = r["trace"]
+    assert t0["m_cand"] == pr["after_block_0"]["m"]
+    assert abs(t0["l_after"] - pr["after_block_0"]["l"]) <= tol
+    assert abs(t0["O"][0] - pr["after_block_0"]["O"]) <= tol
+    assert t1["m_cand"] == pr["block_1"]["m_cand"]
+    assert abs(t1["alpha"] - pr["block_1"]["alpha"]) <= ex["tol_alpha"]
+    assert np.allclose(t1["P"], pr["block_1"]["terms"], atol=ex["tol_alpha"], rtol=0)
+    assert abs(r["l"] - pr["final"]["l"]) <= ex["tol_final_l"]
+    assert abs(r["O"][0] - pr["final"]["O"]) <= ex["tol_final_l"]
+    assert abs(r["out"][0] - pr["final"]["out"]) <= 1e-15
+    # printed slips: the page's rounded values sit close to, not at, the exact ones
+    slip = ex["slip"]
+    exact_ls = E(-8) * (E(-1) + 1)
+    assert abs(t1["l_scaled"] - exact_ls) <= 1e-18
+    assert abs(slip["l_scaled"]["printed"] - exact_ls) <= slip["l_scaled"]["slip_tol"]
+    p, _, _, _ = sr.safe_softmax([1, 2, 3, 10])
+    exact_p = np.array([E(1), E(2), E(3), E(10)]) / (E(1) + E(2) + E(3) + E(10))
+    assert np.allclose(p, exact_p, rtol=1e-14, atol=0)
+    assert np.allclose(slip["softmax"]["printed"], exact_p, rtol=slip["softmax"]["slip_tol_rel"], atol=0)
+
+
+def test_practice_problem_closed_form():
+    cf = _golden()["closed_forms"][0]
+    v = np.asarray(cf["v"], dtype=np.float64)[:, None]
+    r = sr.online_softmax(cf["blocks"], [v[:1], v[1:]])
+    out = (2 * E(-5) + 3) / (E(-5) + 1)
+    lse = 5 + math.log(1 + E(-5))
+    assert abs(r["out"][0] - out) <= 1e-15
+    assert abs(r["lse"] - lse) <= 1e-15
+    # chunk 2 raises the maximum from 0 to 5: alpha = e^-5
+    assert abs(r["trace"][1]["alpha"] - E(-5)) <= 1e-18
+
+
+# ----------------------------------------------------------------------------
+# the worked examples embedded as attention rows (pins the C oracle)
+# ----------------------------------------------------------------------------
+
+def _embed(scores, values, d=4):
+    """Row 0 of Q K^T equals `scores` with scale 1: q0 = e0, k_j = s_j e0;
+    V row j carries values[j] in dimension 0."""
+    n = len(scores)
+    q = np.zeros((1, 1, n, d), dtype=np.float32)
+    k = np.zeros((1, 1, n, d), dtype=np.float32)
+    v = np.zeros((1, 1, n, d), dtype=np.float32)
+    q[0, 0, 0, 0] = 1.0
+    k[0, 0, :, 0] = scores
+    v[0, 0, :, 0] = values
+    return q, k, v
+
+
+@pytest.mark.parametrize("ident", ["blocks_2_4_then_1_3", "blocks_1_2_then_5_3",
+                                   "chunks_1_2_then_3_10_v_ones"])
+def test_examples_through_attention_oracle(ident):
+    ex = _example(ident)
+    s = sum(ex["blocks"], [])
+    vals = ex.get("v", [1.0] * len(s))
+    q, k, v = _embed(s, vals)
+    O, lse, fm = oracle.attention(q, k, v, 1.0)
+    m = max(s)
+    l = sum(E(x - m) for x in s)
+    assert not fm[0, 0, 0]
+    assert abs(lse[0, 0, 0] - (m + math.log(l))) <= 1e-13
+    assert abs(O[0, 0, 0, 0] - sum(E(x - m) * y for x, y in zip(s, vals)) / l) <= 1e-14
+    assert np.all(O[0, 0, 0, 1:] == 0)
+    if ident == "blocks_1_2_then_5_3":
+        assert abs(l - _example(ident)["printed"]["check_sum"]) <= 5e-5
+
+
+def test_practice_problem_through_attention_oracle():
+    q, k, v = _embed([0.0, 5.0], [2.0, 3.0])
+    O, lse, _ = oracle.attention(q, k, v, 1.0)
+    assert abs(O[0, 0, 0, 0] - (2 * E(-5) + 3) / (E(-5) + 1)) <= 1e-14
+    assert abs(lse[0, 0, 0] - (5 + math.log(1 + E(-5)))) <= 1e-14
+
+
+# ----------------------------------------------------------------------------
+# brute force with the naive formula, tiny integer inputs
+# ----------------------------------------------------------------------------
+
+def _naive(q, k, v, scale, causal, mask):
+    """exp(s_j) / sum exp(s_j) written out term by term (no max subtraction;
+    fine at these magnitudes), then the weighted sum of V rows."""
+    B, H, N, d = q.shape
+    O = np.zeros((B, H, N, d))
+    L = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                num = np.zeros(d)
+                den = 0.0
+                for j in range(N):
+                    if causal and j > i:
+                        continue
+                    if mask is not None and mask[b, j] == 0:
+                        continue
+                    s = scale * sum(float(q[b, h, i, t]) * float(k[b, h, j, t]) for t in range(d))
+                    w = math.exp(s)
+                    den += w
+                    num += w * v[b, h, j].astype(np.float64)
+                if den > 0:
+                    O[b, h, i] = num / den
+                    L[b, h, i] = math.log(den)
+    return O, L
+
+
+@pytest.mark.parametrize("N,d,causal,use_mask", [(1, 1, False, False), (3, 2, False, False),
+                                                   (5, 3, True, False), (8, 4, False, True),
+                                                   (7, 4, True, True)])
+def test_brute_force_naive(N, d, causal, use_mask):
+    g = torch.Generator().manual_seed(7 + N * 10 + d)
+    B, H = 2, 2
+    q = torch.randint(-2, 3, (B, H, N, d), generator=g).to(torch.float32).numpy()
+    k = torch.randint(-2, 3, (B, H, N, d), generator=g).to(torch.float32).numpy()
+    v = torch.randint(-3, 4, (B, H, N, d), generator=g).to(torch.float32).numpy()
+    mask = None
+    if use_mask:
+        mask = (torch.rand((B, N), generator=g) > 0.4).to(torch.uint8).numpy()
+        mask[0, :] = 0   # batch 0: every key padded
+    O, L, fm = oracle.attention(q, k, v, 0.5, causal, mask)
+    On, Ln = _naive(q, k, v, 0.5, causal, mask)
+    assert np.array_equal(fm, np.isneginf(Ln))
+    assert np.allclose(O, On, rtol=1e-12, atol=1e-13)
+    fin = ~fm
+    assert np.allclose(L[fin], Ln[fin], rtol=1e-12, atol=1e-13)
+    assert np.all(np.isneginf(L[fm])) and np.all(O[fm] == 0)
+
+
+# ----------------------------------------------------------------------------
+# library routine: torch scaled_dot_product_attention in float64 on the CPU
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 1, 256, 64, False), (1, 4, 2048, 64, False),
+                                            (1, 2, 512, 128, True)])
+def test_against_torch_sdpa_float64(B, H, N, d, causal):
+    q = _rand((B, H, N, d), 11)
+    k = _rand((B, H, N, d), 12)
+    v = _rand((B, H, N, d), 13)
+    scale = 1.0 / math.sqrt(d)
+    qf, kf, vf = (x.astype(np.float32) for x in (q, k, v))
+    O, L, fm = oracle.attention(qf, kf, vf, scale, causal)
+    tq, tk, tv = (torch.from_numpy(x.astype(np.float64)) for x in (qf, kf, vf))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    S = torch.matmul(tq, tk.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        S = S.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), -math.inf)
+    Lref = torch.logsumexp(S, dim=-1)
+    assert not fm.any()
+    assert np.allclose(O, ref.numpy(), rtol=0, atol=1e-10)
+    assert np.allclose(L, Lref.numpy(), rtol=0, atol=1e-10)
+
+
+# ----------------------------------------------------------------------------
+# a different algorithm: the blocked online recurrence, every block size
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,causal,use_mask", [(1, False, False), (5, False, False), (17, True, False),
+                                               (23, False, True), (64, True, True), (64, False, False)])
+def test_recurrence_matches_three_pass_every_block_size(N, causal, use_mask):
+    B, H, d = 2, 2, 8
+    q = _rand((B, H, N, d), 21, 2.0).astype(np.float32)
+    k = _rand((B, H, N, d), 22, 2.0).astype(np.float32)
+    v = _rand((B, H, N, d), 23).astype(np.float32)
+    mask = None
+    if use_mask:
+        lens = torch.tensor([0, N // 2])
+        mask = W.mask_from_lengths(lens, N).numpy()
+    scale = 0.3
+    O, L, fm = oracle.attention(q, k, v, scale, causal, mask)
+    for bc in range(1, N + 1):
+        Or, Lr, fmr = sr.online_attention(q, k, v, scale, causal, mask, block_c=bc)
+        assert np.array_equal(fm, fmr), bc
+        assert np.allclose(Or, O, rtol=1e-12, atol=1e-13), bc
+        fin = ~fm
+        assert np.allclose(Lr[fin], L[fin], rtol=1e-12, atol=1e-13), bc
+        assert np.all(Or[fm] == 0) and np.all(np.isneginf(Lr[fm]))
+
+
+@pytest.mark.parametrize("bc", [1, 2, 3, 7, 64, 256])
+def test_recurrence_in_float32_at_the_tiny_workload(bc):
+    x = W.generate(W.WORKLOADS[0])
+    q, k, v = (x[n].numpy() for n in ("q", "k", "v"))
+    O, L, _ = oracle.attention(q, k, v, x["scale"])
+    Or, Lr, _ = sr.online_attention(q, k, v, x["scale"], block_c=bc, dtype=np.float32)
+    assert np.abs(Or - O).max() <= 1e-5
+    assert np.abs(Lr - L).max() <= 1e-5
+
+
+# ----------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------
+
+def test_shift_invariance_through_an_extra_dimension():
+    """Adding c to every score of a row leaves O unchanged and adds c to LSE:
+    an extra dimension with q = 1 and k = c / scale adds exactly c."""
+    B, H, N, d = 1, 2, 40, 16
+    q = _rand((B, H, N, d), 31).astype(np.float32)
+    k = _rand((B, H, N, d), 32).astype(np.float32)
+    v = _rand((B, H, N, d), 33).astype(np.float32)
+    scale, c = 0.25, 3.0
+    O, L, _ = oracle.attention(q, k, v, scale, True)
+    q2 = np.concatenate([q, np.ones((B, H, N, 1), np.float32)], -1)
+    k2 = np.concatenate([k, np.full((B, H, N, 1), c / scale, np.float32)], -1)
+    v2 = np.concatenate([v, np.zeros((B, H, N, 1), np.float32)], -1)
+    O2, L2, _ = oracle.attention(q2, k2, v2, scale, True)
+    assert np.allclose(O2[..., :d], O, rtol=1e-12, atol=1e-13)
+    assert np.allclose(L2, L + c, rtol=0, atol=1e-12)
+    # score level
+    s = np.array([0.5, -1.0, 2.0, 7.0])
+    p1, _, _, lse1 = sr.safe_softmax(s)
+    p2, _, _, lse2 = sr.safe_softmax(s + 100.0)
+    assert np.allclose(p1, p2, rtol=1e-13, atol=0) and abs(lse2 - lse1 - 100.0) <= 1e-12
+
+
+def test_key_permutation_invariance():
+    B, H, N, d = 2, 2, 33, 8
+    q = _rand((B, H, N, d), 41).astype(np.float32)
+    k = _rand((B, H, N, d), 42).astype(np.float32)
+    v = _rand((B, H, N, d), 43).astype(np.float32)
+    perm = torch.randperm(N, generator=torch.Generator().manual_seed(44)).numpy()
+    O, L, _ = oracle.attention(q, k, v, 0.4)
+    O2, L2, _ = oracle.attention(q, k[:, :, perm], v[:, :, perm], 0.4)
+    assert np.allclose(O, O2, rtol=1e-12, atol=1e-13) and np.allclose(L, L2, rtol=1e-13, atol=0)
+
+
+def test_chunk_order_does_not_matter():
+    s = _rand((50,), 51, 4.0)
+    v = _rand((50, 3), 52)
+    cuts = [0, 7, 8, 20, 33, 50]
+    blocks = [s[a:b] for a, b in zip(cuts, cuts[1:])]
+    vb = [v[a:b] for a, b in zip(cuts, cuts[1:])]
+    fwd = sr.online_softmax(blocks, vb)
+    rev = sr.online_softmax(blocks[::-1], vb[::-1])
+    assert np.allclose(fwd["out"], rev["out"], rtol=1e-13, atol=1e-15)
+    assert abs(fwd["lse"] - rev["lse"]) <= 1e-13
+
+
+def test_safe_softmax_properties():
+    s = np.array([100.0, 102.0, 99.0])   # the overflow example's scores
+    p, m, l, lse = sr.safe_softmax(s)
+    assert m == 102.0
+    assert abs(p.sum() - 1.0) <= 1e-15 and np.all(p > 0) and np.all(p <= 1)
+    e = np.exp(s - m)
+    assert e.max() == 1.0                 # the largest stable term is exp(0)
+    assert np.allclose(p, np.array([E(-2), 1.0, E(-3)]) / (E(-2) + 1 + E(-3)), rtol=1e-15)
+    # magnitudes where exp alone overflows double precision
+    p, m, l, lse = sr.safe_softmax([1000.0, 1001.0])
+    assert np.allclose(p, [1 / (1 + E(1)), E(1) / (1 + E(1))], rtol=1e-15)
+    assert abs(lse - (1001 + math.log(1 + E(-1)))) <= 1e-12
+    q, k, v = _embed([1000.0, 1001.0], [1.0, 3.0])
+    O, L, _ = oracle.attention(q, k, v, 1.0)
+    assert np.isfinite(O).all() and abs(O[0, 0, 0, 0] - (1 + 3 * E(1)) / (1 + E(1))) <= 1e-13
+    assert abs(L[0, 0, 0] - (1001 + math.log(1 + E(-1)))) <= 1e-12
+    # every score must take part in the maximum (a checklist item of the
+    # tutorial's debugging section): with the largest score last and far above
+    # the rest, a maximum that skipped it would overflow exp
+    q, k, v = _embed([0.0, 800.0], [2.0, 5.0])
+    O, L, _ = oracle.attention(q, k, v, 1.0)
+    assert O[0, 0, 0, 0] == 5.0 and L[0, 0, 0] == 800.0
+
+
+def test_merge_of_partial_states_is_the_full_result():
+    s = _rand((40,), 61, 3.0)
+    v = _rand((40, 5), 62)
+    full = sr.online_softmax([s], [v])
+    parts = [sr.online_softmax([s[a:b]], [v[a:b]]) for a, b in [(0, 13), (13, 14), (14, 40)]]
+    st = (parts[0]["m"], parts[0]["l"], parts[0]["O"])
+    for p in parts[1:]:
+        st = sr.merge_states(*st, p["m"], p["l"], p["O"])
+    # the other association order
+    st2 = sr.merge_states(parts[0]["m"], parts[0]["l"], parts[0]["O"],
+                          *sr.merge_states(parts[1]["m"], parts[1]["l"], parts[1]["O"],
+                                           parts[2]["m"], parts[2]["l"], parts[2]["O"]))
+    for m, l, O in (st, st2):
+        assert abs(m - full["m"]) == 0
+        assert abs(l - full["l"]) <= 1e-13 * full["l"]
+        assert np.allclose(O / l, full["out"], rtol=1e-13, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# special cases with known answers
+# ----------------------------------------------------------------------------
+
+def test_special_cases():
+    B, H, N, d = 2, 3, 20, 8
+    q = _rand((B, H, N, d), 71).astype(np.float32)
+    k = _rand((B, H, N, d), 72).astype(np.float32)
+    v = _rand((B, H, N, d), 73).astype(np.float32)
+    # V all ones: O = 1 on every row
+    O, _, _ = oracle.attention(q, k, np.ones_like(v), 0.5, True)
+    assert np.allclose(O, 1.0, rtol=0, atol=1e-14)
+    # causal row 0 sees only key 0: O = v_0, LSE = s_00
+    O, L, _ = oracle.attention(q, k, v, 0.5, True)
+    s00 = 0.5 * (q[:, :, 0].astype(np.float64) * k[:, :, 0]).sum(-1)
+    assert np.allclose(O[:, :, 0], v[:, :, 0], rtol=0, atol=1e-15)
+    assert np.allclose(L[:, :, 0], s00, rtol=0, atol=1e-15)
+    # identical keys: O = mean of the allowed V rows, LSE = s + ln |A_i|
+    k_same = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    O, L, _ = oracle.attention(q, k_same, v, 0.5, True)
+    cm = np.cumsum(v.astype(np.float64), axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    assert np.allclose(O, cm, rtol=1e-12, atol=1e-13)
+    si = 0.5 * (q.astype(np.float64) * k_same[:, :, :1]).sum(-1)
+    assert np.allclose(L, si + np.log(np.arange(1, N + 1))[None, None], rtol=0, atol=1e-12)
+    # a batch whose valid key length is 0: every row fully masked
+    mask = W.mask_from_lengths(torch.tensor([0, 5]), N).numpy()
+    O, L, fm = oracle.attention(q, k, v, 0.5, False, mask)
+    assert fm[0].all() and not fm[1].any()
+    assert np.all(O[0] == 0) and np.all(np.isneginf(L[0]))
+    # padded keys contribute nothing, whatever their values
+    kd, vd = k[1:].copy(), v[1:].copy()
+    kd[:, :, 5:] = 50.0
+    vd[:, :, 5:] = -1e6
+    Od, Ld, _ = oracle.attention(q[1:], kd, vd, 0.5, False, np.array([[1] * 5 + [0] * (N - 5)], np.uint8))
+    assert np.allclose(O[1], Od[0], rtol=1e-12, atol=1e-13) and np.allclose(L[1], Ld[0], rtol=1e-13)
+    Os, Ls, _ = oracle.attention(q[1:, :, :5].copy(), k[1:, :, :5].copy(), v[1:, :, :5].copy(), 0.5)
+    assert np.allclose(O[1, :, :5], Os[0], rtol=1e-12, atol=1e-13)
+    assert np.allclose(L[1, :, :5], Ls[0], rtol=1e-13)
+
+
+def test_sampled_rows_equal_full_result():
+    x = W.generate(W.WORKLOADS[4].with_shape(B=3, H=2, N=96))
+    O, L, fm = oracle.attention(x["q"], x["k"], x["v"], x["scale"], x["causal"], x["mask"])
+    rows = np.array([0, 5, 95, 96, 200, 3 * 2 * 96 - 1])
+    Or, Lr, fmr = oracle.attention(x["q"], x["k"], x["v"], x["scale"], x["causal"], x["mask"], rows=rows)
+    flatO, flatL, flatF = O.reshape(-1, O.shape[-1]), L.reshape(-1), fm.reshape(-1)
+    assert np.array_equal(Or, flatO[rows]) and np.array_equal(fmr, flatF[rows])
+    assert np.array_equal(Lr, flatL[rows])
