@@ -1,0 +1,156 @@
+"""Benchmark of the attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--tile R,C]
+                    [--no-cpu-baseline] [--gpus 1]
+
+A step is one attention forward (one fa_fwd call) over the whole workload,
+inputs already resident in HBM. Prints ONE JSON line. The default workload is
+bf16, causal, d=128, N=8192, B=2, H=32.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X dense MFMA peak for bf16/fp16: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz.
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+HEADLINE = "bf16_causal_n8192_d128"
+KERNEL_PREFIX = "attn_fwd_kernel"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--tile", default=None, help="block_r,block_c")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, x, target_s):
+    """Times the float64 oracle on a bounded random sample of rows of the same
+    workload, on this host's cores; reports nominal TFLOP/s of that sample."""
+    import numpy as np
+    import oracle
+
+    B, H, N, d = w.B, w.H, w.N, w.d
+    rng = np.random.default_rng(123)
+    threads = oracle.max_threads()
+
+    def run(nrows):
+        rows = np.sort(rng.choice(B * H * N, size=nrows, replace=False))
+        flops = 0.0
+        t0 = time.perf_counter()
+        for bh in np.unique(rows // N):
+            b, h = divmod(int(bh), H)
+            rr = rows[(rows // N) == bh] - bh * N
+            mask = None if x["mask"] is None else x["mask"][b:b + 1]
+            oracle.attention(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, h:h + 1], x["v"][b:b + 1, h:h + 1],
+                             x["scale"], x["causal"], mask, rows=rr, nthreads=threads)
+            keys = (rr + 1) if w.causal else np.full(rr.shape, N)
+            flops += float(4.0 * d * keys.sum())
+        return time.perf_counter() - t0, flops, nrows
+
+    dt, fl, n = run(256)
+    n2 = int(min(B * H * N, max(256, 256 * target_s / max(dt, 1e-3))))
+    dt, fl, n = run(n2)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} rows of {w.name} drawn uniformly at random (seed 123), float64 three-pass "
+                      f"oracle, nominal 4*d*(allowed keys) FLOP per row, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over (batch, head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from online_softmax_03_amd import attention as A
+    from online_softmax_03_amd import capi
+    from online_softmax_03_amd import workloads as W
+
+    w = W.BY_NAME[args.workload]
+    x = W.generate(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    mask = None if x["mask"] is None else x["mask"].to(dev)
+    out_dt = W.DTYPES[w.out_dtype]
+    o = torch.empty(q.shape, dtype=out_dt, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    tile = tuple(int(t) for t in args.tile.split(",")) if args.tile else None
+    if tile is None:
+        st, tile = capi.fa_default_tile(w.N, w.d, A._DT[q.dtype], A._DT[out_dt], int(w.causal),
+                                        int(mask is not None))
+        assert st == 0
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        A.attention_fwd(q, k, v, scale=w.scale, causal=w.causal, key_padding_mask=mask,
+                        out_dtype=out_dt, tile=tile, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-launch HIP events on the stream the kernel is launched on
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+
+    flops = w.nominal_flops()
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / avg_launch_s / 1e12
+    peak = PEAK_TFLOPS[w.in_dtype]
+    result = {
+        "metric": "attention fwd TFLOP/s and % of MFMA bf16 peak (causal, d=128, N=8192)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.in_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "key_padding": w.key_padding, "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
+                   "block_r": tile[0], "block_c": tile[1], "flops_per_step": flops},
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": KERNEL_PREFIX, "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

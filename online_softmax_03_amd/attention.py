@@ -1,0 +1,70 @@
+"""Torch-tensor front end of the C ABI.
+
+`attention_fwd` checks devices, dtypes, shapes and contiguity, allocates O
+and LSE with torch (device memory is all torch provides here), and calls
+`fa_fwd_ex` on the current HIP stream. All arithmetic happens in libfa.so.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import capi
+
+_DT = {torch.float32: capi.FA_DTYPE_F32, torch.bfloat16: capi.FA_DTYPE_BF16,
+       torch.float16: capi.FA_DTYPE_F16}
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"fa_fwd failed: {capi.fa_strerror(status)} (status {status})")
+        self.status = status
+
+
+def attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                  causal: bool = False, key_padding_mask: torch.Tensor | None = None,
+                  out_dtype: torch.dtype | None = None, tile=None, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None):
+    """O = softmax(scale * Q K^T, masked) V and LSE for [B, H, N, d] tensors.
+
+    scale defaults to 1/sqrt(d). key_padding_mask: [B, N] bool/uint8 on the
+    same device, True/nonzero = key valid. out_dtype defaults to q.dtype.
+    Returns (o [B, H, N, d], lse [B, H, N] float32).
+    """
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d] with the same shape")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype among float32, bfloat16, float16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DT:
+        raise ValueError("unsupported out_dtype")
+    mask_ptr = None
+    if key_padding_mask is not None:
+        if key_padding_mask.shape != (B, N) or key_padding_mask.device != q.device:
+            raise ValueError("key_padding_mask must be [B, N] on the same device")
+        key_padding_mask = key_padding_mask.to(torch.uint8).contiguous()
+        mask_ptr = key_padding_mask.data_ptr()
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, N, d] tensor of out_dtype")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous [B, H, N] float32 tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = capi.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, N, d, float(scale), int(bool(causal)), mask_ptr, _DT[q.dtype],
+                        _DT[out_dtype], stream, tile)
+    if st != capi.FA_OK:
+        raise FaError(st)
+    return out, lse

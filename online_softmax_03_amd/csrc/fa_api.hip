@@ -1,0 +1,154 @@
+// Host side of the C ABI declared in include/fa.h: argument validation, tile
+// selection, and the kernel launch on the caller's stream. No allocation, no
+// synchronisation, no state.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "attn_fwd_kernel.h"
+#include "fa.h"
+
+namespace {
+
+struct Entry {
+    int d, block_c, nwaves, in_dtype, out_dtype, causal, mask;
+    const void* fn;
+};
+
+#define FA_ENTRY(D, BC, NW, TI, IN, TO, OUT, C, M) \
+    {D, BC, NW, IN, OUT, C, M,                     \
+     reinterpret_cast<const void*>(&fa::attn_fwd_kernel<D, BC, NW, fa::TI, fa::TO, (C) != 0, (M) != 0>)}
+
+#define FA_FLAGS(D, BC, NW, TI, IN, TO, OUT)                                           \
+    FA_ENTRY(D, BC, NW, TI, IN, TO, OUT, 0, 0), FA_ENTRY(D, BC, NW, TI, IN, TO, OUT, 0, 1), \
+        FA_ENTRY(D, BC, NW, TI, IN, TO, OUT, 1, 0), FA_ENTRY(D, BC, NW, TI, IN, TO, OUT, 1, 1)
+
+#define FA_DTYPES(D, BC, NW)                                          \
+    FA_FLAGS(D, BC, NW, BF16, FA_DTYPE_BF16, BF16, FA_DTYPE_BF16),    \
+        FA_FLAGS(D, BC, NW, BF16, FA_DTYPE_BF16, F32, FA_DTYPE_F32),  \
+        FA_FLAGS(D, BC, NW, F16, FA_DTYPE_F16, F16, FA_DTYPE_F16),    \
+        FA_FLAGS(D, BC, NW, F16, FA_DTYPE_F16, F32, FA_DTYPE_F32)
+
+const Entry kTable[] = {
+    FA_DTYPES(128, 64, 4),
+    FA_DTYPES(64, 64, 4),
+};
+
+bool dtype_pair_ok(int in_dtype, int out_dtype) {
+    switch (in_dtype) {
+        case FA_DTYPE_BF16: return out_dtype == FA_DTYPE_BF16 || out_dtype == FA_DTYPE_F32;
+        case FA_DTYPE_F16: return out_dtype == FA_DTYPE_F16 || out_dtype == FA_DTYPE_F32;
+        default: return false;
+    }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+fa_tile default_tile(int d) {
+    (void)d;
+    return fa_tile{128, 64};
+}
+
+const Entry* find(int d, const fa_tile& t, int in_dtype, int out_dtype, int causal, int mask) {
+    if (t.block_r <= 0 || t.block_r % 32 != 0) return nullptr;
+    const int nw = t.block_r / 32;
+    for (const Entry& e : kTable) {
+        if (e.d == d && e.block_c == t.block_c && e.nwaves == nw && e.in_dtype == in_dtype &&
+            e.out_dtype == out_dtype && e.causal == (causal != 0) && e.mask == (mask != 0))
+            return &e;
+    }
+    return nullptr;
+}
+
+fa_tile resolve(int d, const fa_tile* tile) {
+    fa_tile t = default_tile(d);
+    if (tile) {
+        if (tile->block_r != 0) t.block_r = tile->block_r;
+        if (tile->block_c != 0) t.block_c = tile->block_c;
+    }
+    return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_strerror(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "B, H and N must be positive and the sizes must fit";
+        case FA_ERR_HEADDIM: return "head dimension must be 64 or 128";
+        case FA_ERR_DTYPE: return "unsupported (in_dtype, out_dtype) pair";
+        case FA_ERR_SCALE: return "scale must be positive and finite";
+        case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+        case FA_ERR_TILE: return "no kernel for the requested tile shape";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int fa_tile_supported(int d, int in_dtype, int out_dtype, const fa_tile* tile) {
+    const fa_tile t = resolve(d, tile);
+    return find(d, t, in_dtype, out_dtype, 0, 0) ? FA_OK : FA_ERR_TILE;
+}
+
+int fa_default_tile(int N, int d, int in_dtype, int out_dtype, int causal, int has_mask, fa_tile* out) {
+    (void)causal;
+    (void)has_mask;
+    if (!out) return FA_ERR_NULL;
+    if (N <= 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (!dtype_pair_ok(in_dtype, out_dtype)) return FA_ERR_DTYPE;
+    *out = default_tile(d);
+    return FA_OK;
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+              int d, float scale, int causal, const uint8_t* key_padding_mask, int in_dtype,
+              int out_dtype, void* stream, const fa_tile* tile) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (!dtype_pair_ok(in_dtype, out_dtype)) return FA_ERR_DTYPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    const fa_tile t = resolve(d, tile);
+    const Entry* e = find(d, t, in_dtype, out_dtype, causal, key_padding_mask != nullptr);
+    if (!e) return FA_ERR_TILE;
+    // Sizes: every byte offset is computed in 64 bits on the device, but a
+    // row index times the row size must fit in 32 bits, and so must the grid.
+    const long long rows = (long long)B * H * N;
+    const long long n_qtiles = ((long long)N + t.block_r - 1) / t.block_r;
+    const long long grid = (long long)B * H * n_qtiles;
+    if (rows > (1LL << 40) || (long long)N * d * 4 > INT32_MAX || grid > INT32_MAX) return FA_ERR_SHAPE;
+
+    fa::Params prm;
+    prm.q = q;
+    prm.k = k;
+    prm.v = v;
+    prm.o = o;
+    prm.lse = lse;
+    prm.mask = key_padding_mask;
+    prm.B = B;
+    prm.H = H;
+    prm.N = N;
+    prm.n_qtiles = (int)n_qtiles;
+    prm.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    prm.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+    void* args[] = {&prm};
+    const hipError_t err = hipLaunchKernel(e->fn, dim3((unsigned)grid), dim3(e->nwaves * 64), args, 0,
+                                           reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, const uint8_t* key_padding_mask, int in_dtype, int out_dtype,
+           void* stream) {
+    return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask, in_dtype, out_dtype,
+                     stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+"""Parity of the HIP attention forward with the float64 oracle (needs a GPU).
+
+Small shapes are compared element by element on every row; they span several
+tiles and end in ragged tails. The five full-size workloads are compared on
+sampled rows that the oracle computes one by one. Every run pre-fills O and
+LSE with NaN, so an element the kernel fails to write shows up as NaN.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from online_softmax_03_amd import workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+C = {w.name: w for w in W.WORKLOADS}
+TINY, C2, C3, C4, C5 = (w.name for w in W.WORKLOADS)
+
+SMALL = [
+    # (id, base workload, shape overrides, key lengths or None)
+    ("bf16_f32out_d64_n300", C2, dict(B=2, H=3, N=300), None),
+    ("bf16_d64_n200_bf16out", C2, dict(B=1, H=2, N=200, out_dtype="bf16"), None),
+    ("bf16_causal_d128_n333", C3, dict(B=1, H=4, N=333), None),
+    ("bf16_causal_d128_n64", C3, dict(B=2, H=1, N=64), None),
+    ("bf16_noncausal_d128_n190", C3, dict(B=1, H=2, N=190, causal=False), None),
+    ("bf16_causal_long_logits_n700", C4, dict(B=1, H=2, N=700), None),
+    ("f16_keypad_d64_n257", C5, dict(B=6, H=2, N=257), [0, 1, 63, 64, 256, 257]),
+    ("f16_keypad_causal_d128_f32out_n130", C5,
+     dict(B=3, H=2, N=130, d=128, causal=True, out_dtype="f32"), [0, 5, 130]),
+    ("f16_d64_n1", C5, dict(B=1, H=1, N=1, key_padding=False), None),
+    ("bf16_causal_d64_n2", C2, dict(B=1, H=1, N=2, causal=True), None),
+    ("bf16_d128_n31", C3, dict(B=1, H=1, N=31), None),
+    ("f16_d64_n33_keypad", C5, dict(B=2, H=1, N=33), [32, 33]),
+]
+
+
+@pytest.mark.parametrize("ident,base,over,lens", SMALL, ids=[s[0] for s in SMALL])
+def test_small_shapes_every_row(ident, base, over, lens):
+    w = C[base].with_shape(**over)
+    x = W.generate(w, lens=None if lens is None else torch.tensor(lens, dtype=torch.int64))
+    U.log(f"case {ident}: B,H,N,d={w.B},{w.H},{w.N},{w.d} {w.in_dtype}->{w.out_dtype} causal={w.causal}")
+    U.check_full(x, what=ident)
+
+
+WORKED = [
+    # scores, values: the pages' worked examples as row 0 of an attention
+    ([2.0, 4.0, 1.0, 3.0], [1.0, 1.0, 1.0, 1.0]),
+    ([1.0, 2.0, 5.0, 3.0], [1.0, -1.0, 2.0, 0.5]),
+    ([1.0, 2.0, 3.0, 10.0], [1.0, 1.0, 1.0, 1.0]),
+    ([0.0, 5.0], [2.0, 3.0]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", range(len(WORKED)))
+def test_worked_examples_as_attention(case, dtype):
+    """q_0 = e_0, k_j = s_j e_0, scale 1: row 0's scores are the example's.
+    All values are exact in bf16 and fp16. LSE and O follow in closed form."""
+    s, vals = WORKED[case]
+    n, d = len(s), 64
+    dt = W.DTYPES[dtype]
+    q = torch.zeros(1, 1, n, d)
+    k = torch.zeros(1, 1, n, d)
+    v = torch.zeros(1, 1, n, d)
+    q[0, 0, 0, 0] = 1.0
+    k[0, 0, :, 0] = torch.tensor(s)
+    v[0, 0, :, 0] = torch.tensor(vals)
+    x = dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), mask=None, scale=1.0, causal=False,
+             in_dtype=dtype, out_dtype="f32")
+    O, L = U.run_gpu(x)
+    m = max(s)
+    l = sum(math.exp(t - m) for t in s)
+    assert abs(L[0, 0, 0] - (m + math.log(l))) <= U.LSE_TOL
+    ref = sum(math.exp(t - m) * y for t, y in zip(s, vals)) / l
+    assert abs(O[0, 0, 0, 0] - ref) <= U.O_TOL[dtype]
+    assert np.all(O[0, 0, 0, 1:] == 0)
+    U.check_full(x, what=f"worked example {case} {dtype}")
+
+
+@pytest.mark.parametrize("name", [C2, C3, C4, C5])
+def test_full_size_sampled_rows(name):
+    w = C[name]
+    U.log(f"case {name}: full size B,H,N,d={w.B},{w.H},{w.N},{w.d}")
+    x = W.generate(w)
+    rows = U.sample_rows(w.B, w.H, w.N, 96, seed=5, causal=w.causal)
+    if w.key_padding:
+        # rows of the batch with no valid key, and of the one with no padding
+        for b in (0, w.B - 1):
+            rows = np.union1d(rows, [(b * w.H) * w.N + i for i in (0, 7, w.N - 1)])
+    O, L, _ = U.check_sampled(x, rows, what=name)
+    assert not np.isnan(O).any() and not np.isnan(L).any()
+    if w.key_padding:
+        lens = x["lens"].numpy()
+        dead_b = lens == 0
+        assert np.all(np.isneginf(L[dead_b])) and np.all(O[dead_b] == 0)
+        assert not np.isneginf(L[~dead_b]).any()
+    if w.causal:
+        # row 0 of every head attends to key 0 only: O = v_0, LSE = scale*q_0.k_0
+        v0 = x["v"][:, :, 0].double().numpy()
+        assert np.abs(O[:, :, 0] - v0).max() <= U.O_TOL[w.in_dtype]
+
+
+def test_nondefault_stream_and_repeat():
+    w = C[C2].with_shape(B=1, H=2, N=256)
+    x = W.generate(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        O1, L1 = U.run_gpu(x)
+    O2, L2 = U.run_gpu(x)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
