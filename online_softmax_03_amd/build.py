@@ -27,6 +27,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops stay off: the compiler would otherwise form them
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in architectural VGPRs: the online-softmax
+    # rescale and the epilogue touch them with VALU ops, which cannot read
+    # AGPRs without a copy
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

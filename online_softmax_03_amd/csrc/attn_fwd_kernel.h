@@ -6,27 +6,39 @@
 // looped over; every query row keeps its own state, "在线Softmax算法解析"
 // section 3.3). Per tile:
 //
-//   1. K_j and V_j land in LDS straight from HBM (global_load_lds_dwordx4,
+//   1. K_j and V_j land in LDS straight from HBM (buffer_load_dwordx4 ... lds,
 //      16 bytes per lane, coalesced), double-buffered so the next tile's load
-//      overlaps this tile's math.
+//      overlaps this tile's math. Rows past the end of the sequence fall
+//      outside the buffer resource and read as zero.
 //   2. S^T = K_j * Q^T on v_mfma_f32_32x32x16 (bf16/fp16 in, fp32 out). The
 //      transposed product puts one query per lane column: lane l holds query
 //      l%32 and 16 of the tile's 32 keys per 32-key block, the other 16 sit in
 //      lane l^32. Row max and row sum are then in-lane reductions plus a single
 //      v_permlane32_swap, instead of a 32-lane butterfly.
-//   3. Mask (causal diagonal, key padding, sequence tail) by writing -inf.
+//   3. Mask (causal diagonal, key range, padded keys) by writing -inf.
 //   4. Online update in raw score units with the scale folded into exp2
-//      ("Online Softmax 算法详解" sections 4.3, 4.5, 5): m_new = max(m, rowmax),
-//      alpha = 2^((m - m_new)*c), l = alpha*l + sum P, P = 2^(s*c - m_new*c)
-//      as one FMA plus v_exp_f32, c = scale*log2(e). The -inf guard of section
-//      7.1 uses 0 as the subtrahend when m_new is still -inf. O is rescaled
-//      only when some row maximum in the wave actually moved (the conditional
-//      rescale of "在线Softmax算法解析" section 2.1, step 3).
+//      ("Online Softmax 算法详解" sections 4.3, 4.5, 5): each row keeps a
+//      reference maximum m; with m_new = max(m, rowmax) the state is rescaled,
+//      alpha = 2^((m - m_new)*c), l *= alpha, O *= alpha, m = m_new, and then
+//      P = 2^(s*c - m*c) as one FMA plus v_exp_f32, l += sum P, with
+//      c = scale*log2(e). The rescale is conditional, as in step 3 of
+//      "在线Softmax算法解析" section 2.1, but with a margin: it runs only when
+//      some row of the wave saw its maximum grow by more than kRescaleLog2
+//      (in log2 units) since the last rescale. Until then P may exceed 1 by up
+//      to 2^kRescaleLog2, which bf16, fp16 and the fp32 accumulators hold
+//      easily, and the result is unchanged because any reference point gives
+//      the same O/l (the shift invariance the pages' exactness proofs rest on).
+//      The -inf guard of "Online Softmax 算法详解" section 7.1 uses 0 as the
+//      subtrahend while m is still -inf.
 //   5. P is rounded to bf16/fp16 in registers and fed straight back as the B
 //      operand of O^T += V_j^T * P^T: the MFMA result layout of S^T matches the
 //      operand layout up to a fixed permutation of keys inside each 16-key
 //      group, and the V^T operand is read from the row-major V tile with
 //      ds_read_b64_tr_b16 in that same key order. No LDS round trip for P.
+//      The row sum l is accumulated from the fp32 P before rounding (as the
+//      deferred row sum of "Online Softmax 算法详解" section 4.6 is): summing
+//      the rounded values instead would put bf16's 2^-9 relative error
+//      straight into the LSE.
 //
 // After the last tile: the two lane halves' row sums are added (the deferred
 // cross-lane reduce of "Online Softmax 算法详解" section 4.6), inv = 1/l with the
@@ -51,7 +63,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 #define FA_LDS __attribute__((address_space(3)))
-#define FA_GLOBAL __attribute__((address_space(1)))
 
 // Element tags.
 struct BF16 { static constexpr int kBytes = 2; };
@@ -72,6 +83,11 @@ struct Params {
 };
 
 constexpr float kLn2 = 0.69314718055994530942f;
+// Largest growth of a row maximum, in log2 units of the exponent, tolerated
+// before the state is rescaled: P stays below 2^8 = 256.
+constexpr float kRescaleLog2 = 8.0f;
+// Word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle.
+constexpr int kBufferFlags = 0x00020000;
 
 // ---------------------------------------------------------------- helpers
 
@@ -88,6 +104,12 @@ template <>
 __device__ __forceinline__ f32x16 mfma32x32x16<F16>(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// fp32 inputs: one k-pair per instruction. A: lane l holds A[l%32][l/32];
+// B: lane l holds B[l/32][l%32]; the result layout is that of the 16-bit forms.
+__device__ __forceinline__ f32x16 mfma32x32x2_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
 // Two floats rounded to nearest-even into one packed 32-bit register.
@@ -119,13 +141,15 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS tile layout: row-major [B_c][D] with the 16-byte chunk index XORed by a
-// row-dependent pattern, so that the K operand reads (16 rows x one chunk per
-// 16 lanes) and the V transpose reads (4 rows x 4 chunks per 16 lanes) hit
-// distinct bank groups.
-template <int D>
+// LDS tile layout: row-major [B_c][row bytes] with the 16-byte chunk index
+// XORed by a row-dependent pattern, so that the K operand reads (16 rows x one
+// chunk per 16 lanes) and the V transpose reads (4 rows x 4 chunks per 16
+// lanes) hit distinct bank groups.
+//   CH = 8 chunks per row (bf16/fp16, d = 64):  ((row>>1)&1)<<2 | (row>>2)&3
+//   CH >= 16 (bf16/fp16 d = 128, fp32):        (row&3)<<2 | (row>>2)&3
+template <int CH>
 __device__ __forceinline__ constexpr int swz(int row) {
-    if constexpr (D == 128) {
+    if constexpr (CH >= 16) {
         return ((row & 3) << 2) | ((row >> 2) & 3);
     } else {
         return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
@@ -158,60 +182,77 @@ __device__ __forceinline__ void store_row4<F16>(char* dst, const float* v4, floa
     *reinterpret_cast<u32x2*>(dst) = r;
 }
 
-// First and last index j in [0, n) with row[j] != 0, over the whole
-// workgroup. Returns {INT32_MAX, -1} when there is none.
+// Valid-key extent of one mask row over [0, n): the first and last index
+// with row[j] != 0 and the number of such indices, reduced over the whole
+// workgroup. first = INT32_MAX, last = -1 when there is none.
 template <int NT>
-__device__ __forceinline__ void mask_extent(const uint8_t* row, int n, int* first, int* last) {
-    __shared__ int s_first[NT / 64], s_last[NT / 64];
-    int f = 0x7fffffff, l = -1;
+__device__ __forceinline__ void mask_extent(const uint8_t* row, int n, int* first, int* last,
+                                            int* count) {
+    __shared__ int s_red[3][NT / 64];
+    int f = 0x7fffffff, l = -1, cnt = 0;
     for (int j = threadIdx.x; j < n; j += NT) {
         if (row[j] != 0) {
             f = min(f, j);
             l = max(l, j);
+            ++cnt;
         }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         f = min(f, __shfl_xor(f, off));
         l = max(l, __shfl_xor(l, off));
+        cnt += __shfl_xor(cnt, off);
     }
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
-        s_first[w] = f;
-        s_last[w] = l;
+        s_red[0][w] = f;
+        s_red[1][w] = l;
+        s_red[2][w] = cnt;
     }
     __syncthreads();
-    f = s_first[0];
-    l = s_last[0];
+    f = s_red[0][0];
+    l = s_red[1][0];
+    cnt = s_red[2][0];
 #pragma unroll
     for (int i = 1; i < NT / 64; ++i) {
-        f = min(f, s_first[i]);
-        l = max(l, s_last[i]);
+        f = min(f, s_red[0][i]);
+        l = max(l, s_red[1][i]);
+        cnt += s_red[2][i];
     }
     *first = f;
     *last = l;
+    *count = cnt;
 }
 
 // ---------------------------------------------------------------- kernel
 
 template <int D, int BC, int NW, typename TI, typename TO, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
+    // The body uses device-only types (buffer resources), so the host pass,
+    // which only needs the launch stub, does not see it.
+#if defined(__HIP_DEVICE_COMPILE__)
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BC % 32 == 0 && BC >= 32 && BC <= 128, "key tile");
-    static_assert(TI::kBytes == 2, "16-bit inputs on this path");
+    constexpr bool kF32 = TI::kBytes == 4;  // fp32 inputs: fp32 MFMA, P kept in fp32
+    static_assert(!kF32 || TO::kBytes == 4, "fp32 inputs write fp32 output");
     constexpr int NT = NW * 64;
     constexpr int BR = NW * 32;          // query rows per workgroup
     constexpr int NKB = BC / 32;         // 32-key blocks per tile
     constexpr int NDC = D / 16;          // 16-wide slices of d (QK contraction steps)
     constexpr int NDB = D / 32;          // 32-wide blocks of d in O^T
-    constexpr int CH = D / 8;            // 16-byte chunks per row
-    constexpr int ROWB = D * 2;          // bytes per row
+    constexpr int EB = TI::kBytes;       // bytes per input element
+    constexpr int ROWB = D * EB;         // bytes per row
+    constexpr int CH = ROWB / 16;        // 16-byte chunks per row
     constexpr int TILEB = BC * ROWB;     // bytes per K or V tile
     constexpr int RPI = 1024 / ROWB;     // tile rows per 1 KB wave load
     constexpr int LOADS = TILEB / 1024;  // wave loads per tensor per tile
     constexpr int LPW = (LOADS + NW - 1) / NW;
 
-    __shared__ __attribute__((aligned(1024))) char smem[2][2][TILEB];  // [buffer][K, V]
+    // Two tile buffers, each K then V. They are distinct objects (not one
+    // array indexed by parity) so the compiler can see that this tile's LDS
+    // reads never alias the next tile's in-flight DMA writes.
+    __shared__ __attribute__((aligned(1024))) char buf0[2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) char buf1[2 * TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -233,117 +274,181 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     const int qw0 = q0 + wave * 32;
 
     const size_t head = (size_t)bh * (size_t)N * D;
-    const char* qg = reinterpret_cast<const char*>(p.q) + head * 2;
-    const char* kg = reinterpret_cast<const char*>(p.k) + head * 2;
-    const char* vg = reinterpret_cast<const char*>(p.v) + head * 2;
+    const char* qg = reinterpret_cast<const char*>(p.q) + head * EB;
+    const char* kg = reinterpret_cast<const char*>(p.k) + head * EB;
+    const char* vg = reinterpret_cast<const char*>(p.v) + head * EB;
 
-    // Key range this workgroup must visit.
-    int kv_begin = 0;
-    int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+    // Keys [key_lo, key_hi) may be valid: the whole sequence, or the extent of
+    // the key mask's valid entries. When those entries are contiguous (a
+    // padding mask), the range test below is the whole mask; otherwise every
+    // key is also looked up in the mask.
+    int key_lo = 0, key_hi = N;
+    bool mask_general = false;
     const uint8_t* mrow = MASK ? p.mask + (size_t)b * N : nullptr;
     if constexpr (MASK) {
-        int first, last;
-        mask_extent<NT>(mrow, kv_end, &first, &last);
+        int first, last, count;
+        mask_extent<NT>(mrow, N, &first, &last, &count);
         if (last < 0) {
-            kv_end = 0;
+            key_hi = 0;
         } else {
-            kv_begin = (first / BC) * BC;
-            kv_end = last + 1;
+            key_lo = first;
+            key_hi = last + 1;
+            mask_general = count != key_hi - key_lo;
         }
     }
+    const int kv_begin = (key_lo / BC) * BC;
+    const int kv_end = CAUSAL ? min(key_hi, q0 + BR) : key_hi;
     const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + BC - 1) / BC : 0;
 
-    // Issue one tile's K and V loads into LDS buffer `buf`. Wave load R fills
-    // bytes [R*1024, R*1024+1024) of the tile: lane s writes slot s of that
-    // range, i.e. row R*RPI + s/CH, physical chunk s%CH, which holds logical
-    // chunk (s%CH) ^ swz(row). Rows past N read row N-1 (finite data; those
-    // keys are masked).
-    auto issue_tile = [&](int tile, int buf) {
+    // V halves of both buffers start at zero so that a row the DMA leaves
+    // untouched can never inject a non-finite value into P*V.
+    {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int off = tid * 16; off < TILEB; off += NT * 16) {
+            *reinterpret_cast<FA_LDS u32x4*>((FA_LDS char*)buf0 + TILEB + off) = z;
+            *reinterpret_cast<FA_LDS u32x4*>((FA_LDS char*)buf1 + TILEB + off) = z;
+        }
+        __syncthreads();
+    }
+
+    // DMA geometry. Wave load R of a tile fills bytes [R*1024, R*1024+1024):
+    // lane s writes slot s, i.e. tile row R*RPI + s/CH at physical chunk s%CH,
+    // which holds logical chunk (s%CH) ^ swz(row). lane_off[ii] is that row
+    // and chunk as a byte offset from the tile's first row.
+    u32 lane_off[LPW];
+#pragma unroll
+    for (int ii = 0; ii < LPW; ++ii) {
+        const int R = wave + ii * NW;
+        const int trow = R * RPI + lane / CH;
+        lane_off[ii] = (u32)(trow * ROWB + (((lane % CH) ^ swz<CH>(trow)) * 16));
+    }
+    auto issue_tile = [&](int tile, char* buf) {
         const int k0 = kv_begin + tile * BC;
+        const int bytes = (N - k0) * ROWB;  // rows past N are out of range: read as 0
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kg + (size_t)k0 * ROWB), 0, bytes, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vg + (size_t)k0 * ROWB), 0, bytes, kBufferFlags);
 #pragma unroll
         for (int ii = 0; ii < LPW; ++ii) {
             const int R = wave + ii * NW;
             if (LOADS % NW != 0 && R >= LOADS) break;
-            const int trow = R * RPI + lane / CH;
-            const int row = min(k0 + trow, N - 1);
-            const int chunk = (lane % CH) ^ swz<D>(trow);
-            const size_t off = (size_t)row * ROWB + chunk * 16;
-            __builtin_amdgcn_global_load_lds((const FA_GLOBAL void*)(kg + off),
-                                             (FA_LDS void*)(&smem[buf][0][R * 1024]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const FA_GLOBAL void*)(vg + off),
-                                             (FA_LDS void*)(&smem[buf][1][R * 1024]), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(buf + R * 1024), 16, lane_off[ii],
+                                                     0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(buf + TILEB + R * 1024), 16,
+                                                     lane_off[ii], 0, 0, 0);
         }
     };
 
-    // Q^T as the B operand: lane l holds query l%32, d = 16*dc + 8*(l/32) .. +7.
-    u32x4 qop[NDC];
+    // Q^T as the B operand. 16-bit inputs: lane l holds query l%32 and
+    // d = 16*dc + 8*(l/32) .. +7 in qop[dc]. fp32 inputs: lane l holds
+    // d = (l/32)*D/2 + t in qf[t], and instruction t contracts the pair
+    // (t, D/2 + t) of d values.
+    u32x4 qop[kF32 ? 1 : NDC];
+    float qf[kF32 ? D / 2 : 1];
     {
         const int qr = min(qw0 + col, N - 1);
-        const char* src = qg + (size_t)qr * ROWB + hh * 16;
+        if constexpr (kF32) {
+            const char* src = qg + (size_t)qr * ROWB + hh * (ROWB / 2);
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) qop[dc] = *reinterpret_cast<const u32x4*>(src + dc * 32);
+            for (int i = 0; i < D / 8; ++i) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(src + i * 16);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) qf[4 * i + j] = x[j];
+            }
+        } else {
+            const char* src = qg + (size_t)qr * ROWB + hh * 16;
+#pragma unroll
+            for (int dc = 0; dc < NDC; ++dc) qop[dc] = *reinterpret_cast<const u32x4*>(src + dc * 32);
+        }
     }
 
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-    float m_run = -INFINITY;  // running row max, raw q.k units
+    float m_run = -INFINITY;  // reference row maximum, raw q.k units
     float l_run = 0.f;        // this lane's share of the running row sum
     const float c = p.c;
     const bool wave_live = qw0 < N;
+    const int qq = qw0 + col;  // this lane's query
 
-    // Per-lane geometry of the V^T transpose reads (see the PV step).
-    const int g16 = lane >> 4;
-    const int tr_r = (lane & 15) >> 2;   // which of 4 consecutive keys this lane addresses
-    const int tr_c = lane & 3;           // which 4-wide d slice it addresses
-    const int tr_dsub = g16 & 1;         // which 16 of the 32 d values the group covers
-    const int sw_k = swz<D>(col) ^ hh;   // K operand: chunk (2*dc + hh) ^ swz(row)
+    // K operand rows are 32*kb + col: one chunk XOR per lane.
+    const int sw_col = swz<CH>(col);
+    // V^T transpose reads (16-bit path): within each 16-lane group, lane
+    // 4r + c addresses tile row key0 + r at d offset dbase + 4c, where key0 =
+    // 32kb + 16t + 8*half + 4*hh and dbase = 32db + 16*(group & 1). The XOR
+    // pattern of those rows does not depend on kb or t, so each (db, half)
+    // address is one per-lane offset plus a constant.
+    const int tr_r = (lane & 15) >> 2;
+    const int tr_c = lane & 3;
+    const int tr_dsub = (lane >> 4) & 1;
+    u32 v_off[kF32 ? 1 : NDB][2];
+    if constexpr (!kF32) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int row = 8 * half + 4 * hh + tr_r;
+                const int chunk = 4 * db + 2 * tr_dsub + (tr_c >> 1);
+                v_off[db][half] = (u32)(row * ROWB + ((chunk ^ swz<CH>(row)) << 4) + (tr_c & 1) * 8);
+            }
+    }
 
-    if (n_tiles > 0) issue_tile(0, 0);
-
-    for (int it = 0; it < n_tiles; ++it) {
-        const int buf = it & 1;
-        const int k0 = kv_begin + it * BC;
-        wait_vmcnt0();     // this wave's loads of tile `it` have landed
-        __syncthreads();   // ... everyone's, and tile it-1 is no longer read
-        if (it + 1 < n_tiles) issue_tile(it + 1, buf ^ 1);
-
+    auto compute_tile = [&](int tile, const char* buf) {
+        const int k0 = kv_begin + tile * BC;
         // Waves whose queries all precede this tile's first key have nothing to do.
-        const bool need = wave_live && (!CAUSAL || k0 <= qw0 + 31);
-        if (!need) continue;
-
-        const char* kt = &smem[buf][0][0];
-        const char* vt = &smem[buf][1][0];
+        if (!wave_live || (CAUSAL && k0 > qw0 + 31)) return;
+        const FA_LDS char* kt = (const FA_LDS char*)buf;
+        const FA_LDS char* vt = (const FA_LDS char*)buf + TILEB;
 
         // ---- S^T = K_j Q^T
         f32x16 s[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+        if constexpr (kF32) {
+            // lane (col, hh) reads K[32kb + col][hh*D/2 + 4i .. +3] for 4 instructions
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
+            for (int i = 0; i < D / 8; ++i) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const int row = kb * 32 + col;
-                const int chunk = (2 * dc) ^ sw_k;
-                const u32x4 a = *reinterpret_cast<const FA_LDS u32x4*>(
-                    (const FA_LDS char*)kt + row * ROWB + chunk * 16);
-                s[kb] = mfma32x32x16<TI>(a, qop[dc], s[kb]);
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const int chunk = (hh * (D / 8) + i) ^ sw_col;
+                    const f32x4 a4 = *reinterpret_cast<const FA_LDS f32x4*>(
+                        kt + (kb * 32 + col) * ROWB + chunk * 16);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) s[kb] = mfma32x32x2_f32(a4[j], qf[4 * i + j], s[kb]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int dc = 0; dc < NDC; ++dc) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const int chunk = (2 * dc + hh) ^ sw_col;
+                    const u32x4 a =
+                        *reinterpret_cast<const FA_LDS u32x4*>(kt + (kb * 32 + col) * ROWB + chunk * 16);
+                    s[kb] = mfma32x32x16<TI>(a, qop[dc], s[kb]);
+                }
             }
         }
 
-        // ---- masks: keys past the range, the causal diagonal, padded keys
+        // ---- masks. Register r of block kb is key k0 + 4*hh + kb*32 +
+        // 8*(r/4) + r%4; the constant part is compared against per-lane limits.
+        const bool edge_lo = k0 < key_lo;
+        const bool edge_hi = k0 + BC > kv_end;
         const bool diag = CAUSAL && (k0 + BC - 1 > qw0);
-        const bool tail = k0 + BC > kv_end;
-        if (MASK || diag || tail) {
-            const int qq = qw0 + col;
+        if (edge_lo || edge_hi || diag || (MASK && mask_general)) {
+            const int base = k0 + 4 * hh;
+            int hi = min(key_hi, kv_end) - 1 - base;  // last allowed key, relative
+            if (CAUSAL) hi = min(hi, qq - base);
+            const int lo = key_lo - base;             // first allowed key, relative
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    bool ok = key < kv_end;
-                    if (CAUSAL) ok = ok && key <= qq;
-                    if (MASK) ok = ok && mrow[min(key, N - 1)] != 0;
+                    const int rel = kb * 32 + 8 * (r >> 2) + (r & 3);
+                    bool ok = rel <= hi && rel >= lo;
+                    if (MASK && mask_general) ok = ok && mrow[min(base + rel, N - 1)] != 0;
                     s[kb][r] = ok ? s[kb][r] : -INFINITY;
                 }
             }
@@ -357,63 +462,96 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         mx = pair_max(mx);
         const float m_new = fmaxf(m_run, mx);
-        const float ref = (m_new == -INFINITY) ? 0.f : m_new * c;
-        const float alpha = __builtin_amdgcn_exp2f(m_run * c - ref);
-        float rs = 0.f;
+        // (m_new - m_run)*c is +inf on a row's first live tile (m_run = -inf)
+        // and NaN while the row has seen only masked keys (no rescale needed).
+        if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kRescaleLog2) != 0) {
+            // rows still at -inf (only masked keys so far) get alpha = 2^-inf = 0
+            const float alpha =
+                __builtin_amdgcn_exp2f(m_run * c - ((m_new == -INFINITY) ? 0.f : m_new * c));
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float ref = (m_run == -INFINITY) ? 0.f : m_run * c;
+        float rs0 = 0.f, rs1 = 0.f;  // two chains for the fp32 row sum
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -ref));
-                s[kb][r] = e;
-                rs += e;
+                s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -ref));
+                if (r & 1) rs1 += s[kb][r];
+                else rs0 += s[kb][r];
             }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-        }
+        l_run += rs0 + rs1;
 
-        // ---- P^T as the B operand: 16-key group t of block kb is registers 8t..8t+7
-        u32x4 pb[NKB][2];
+        if constexpr (kF32) {
+            // ---- O^T += V_j^T P^T in fp32: register r of S^T block kb is key
+            // 32kb + 8(r/4) + 4*hh + r%4, the k = hh slot of instruction r; the
+            // A operand is V[that key][32db + col].
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+            for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    pb[kb][t][j] = pack2<TI>(s[kb][8 * t + 2 * j], s[kb][8 * t + 2 * j + 1]);
+                    for (int db = 0; db < NDB; ++db) {
+                        const int chunk = (8 * db + (col >> 2)) ^ swz<CH>(key);
+                        const float a = *reinterpret_cast<const FA_LDS float*>(
+                            vt + key * ROWB + chunk * 16 + (col & 3) * 4);
+                        acc[db] = mfma32x32x2_f32(a, s[kb][r], acc[db]);
+                    }
+                }
+            }
+        } else {
+            // ---- P^T as the B operand: 16-key group t of block kb is registers 8t..8t+7
+            u32x4 pb[NKB][2];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pb[kb][t][j] = pack2<TI>(s[kb][8 * t + 2 * j], s[kb][8 * t + 2 * j + 1]);
 
-        // ---- O^T += V_j^T P^T. Register j of the B operand above is key
-        // 16t + 8(j/4) + 4*hh + j%4 of the block; the A operand must hold
-        // V[that key][d = l%32] in the same slot. Two ds_read_b64_tr_b16 give
-        // it: within each 16-lane group, lane 4r+c addresses V[key0 + r][dbase
-        // + 4c .. +3], and after the transpose lane i holds V[key0 .. key0+3]
-        // [dbase + i].
+            // ---- O^T += V_j^T P^T. Register j of the B operand above is key
+            // 16t + 8(j/4) + 4*hh + j%4 of the block; the A operand must hold
+            // V[that key][d = l%32] in the same slot. Two ds_read_b64_tr_b16
+            // give it: after the transpose, lane i of a 16-lane group holds
+            // V[key0 .. key0+3][dbase + i].
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+            for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int row0 = kb * 32 + t * 16 + 4 * hh + tr_r;
-                const int row1 = row0 + 8;
+                for (int t = 0; t < 2; ++t) {
+                    const int rowc = (kb * 32 + t * 16) * ROWB;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int chunk = 4 * db + 2 * tr_dsub + (tr_c >> 1);
-                    const int within = (tr_c & 1) * 8;
-                    const FA_LDS char* a0 = (const FA_LDS char*)vt + row0 * ROWB +
-                                            ((chunk ^ swz<D>(row0)) << 4) + within;
-                    const FA_LDS char* a1 = (const FA_LDS char*)vt + row1 * ROWB +
-                                            ((chunk ^ swz<D>(row1)) << 4) + within;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)a0);
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)a1);
-                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-                    const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-                    const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                    acc[db] = mfma32x32x16<TI>(a, pb[kb][t], acc[db]);
+                    for (int db = 0; db < NDB; ++db) {
+                        const i16x4 lo =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vt + rowc + v_off[db][0]));
+                        const i16x4 hi =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vt + rowc + v_off[db][1]));
+                        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+                        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+                        const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+                        acc[db] = mfma32x32x16<TI>(a, pb[kb][t], acc[db]);
+                    }
                 }
             }
         }
+    };
+
+    // Main loop, unrolled by two so each half names its buffer statically.
+    if (n_tiles > 0) issue_tile(0, buf0);
+    for (int it = 0; it < n_tiles; it += 2) {
+        wait_vmcnt0();     // this wave's loads of tile `it` have landed
+        __syncthreads();   // ... everyone's, and tile it-1 (buffer 1) is no longer read
+        if (it + 1 < n_tiles) issue_tile(it + 1, buf1);
+        compute_tile(it, buf0);
+        if (it + 1 >= n_tiles) break;
+        wait_vmcnt0();
+        __syncthreads();
+        if (it + 2 < n_tiles) issue_tile(it + 2, buf0);
+        compute_tile(it + 1, buf1);
     }
 
     // ---- finalize and store
@@ -421,7 +559,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     const bool dead = !(l_tot > 0.f);  // no allowed key (sum 0) or NaN
     const float inv = dead ? 0.f : 1.f / l_tot;
     const float lse = dead ? -INFINITY : (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    const int qq = qw0 + col;
     if (qq < N) {
         char* orow = reinterpret_cast<char*>(p.o) + (head + (size_t)qq * D) * TO::kBytes;
 #pragma unroll
@@ -435,6 +572,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
             }
         if (hh == 0) p.lse[(size_t)bh * N + qq] = lse;
     }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 }  // namespace fa

@@ -6,39 +6,25 @@
 
 #include <hip/hip_runtime.h>
 
-#include "attn_fwd_kernel.h"
 #include "fa.h"
+#include "fa_table.h"
+
+namespace fa {
+extern const EntryList kList_d128_bf16, kList_d128_f16, kList_d64_bf16, kList_d64_f16, kList_f32;
+}
 
 namespace {
 
-struct Entry {
-    int d, block_c, nwaves, in_dtype, out_dtype, causal, mask;
-    const void* fn;
-};
+using fa::Entry;
 
-#define FA_ENTRY(D, BC, NW, TI, IN, TO, OUT, C, M) \
-    {D, BC, NW, IN, OUT, C, M,                     \
-     reinterpret_cast<const void*>(&fa::attn_fwd_kernel<D, BC, NW, fa::TI, fa::TO, (C) != 0, (M) != 0>)}
-
-#define FA_FLAGS(D, BC, NW, TI, IN, TO, OUT)                                           \
-    FA_ENTRY(D, BC, NW, TI, IN, TO, OUT, 0, 0), FA_ENTRY(D, BC, NW, TI, IN, TO, OUT, 0, 1), \
-        FA_ENTRY(D, BC, NW, TI, IN, TO, OUT, 1, 0), FA_ENTRY(D, BC, NW, TI, IN, TO, OUT, 1, 1)
-
-#define FA_DTYPES(D, BC, NW)                                          \
-    FA_FLAGS(D, BC, NW, BF16, FA_DTYPE_BF16, BF16, FA_DTYPE_BF16),    \
-        FA_FLAGS(D, BC, NW, BF16, FA_DTYPE_BF16, F32, FA_DTYPE_F32),  \
-        FA_FLAGS(D, BC, NW, F16, FA_DTYPE_F16, F16, FA_DTYPE_F16),    \
-        FA_FLAGS(D, BC, NW, F16, FA_DTYPE_F16, F32, FA_DTYPE_F32)
-
-const Entry kTable[] = {
-    FA_DTYPES(128, 64, 4),
-    FA_DTYPES(64, 64, 4),
-};
+const fa::EntryList* const kLists[] = {&fa::kList_d128_bf16, &fa::kList_d128_f16, &fa::kList_d64_bf16,
+                                       &fa::kList_d64_f16, &fa::kList_f32};
 
 bool dtype_pair_ok(int in_dtype, int out_dtype) {
     switch (in_dtype) {
         case FA_DTYPE_BF16: return out_dtype == FA_DTYPE_BF16 || out_dtype == FA_DTYPE_F32;
         case FA_DTYPE_F16: return out_dtype == FA_DTYPE_F16 || out_dtype == FA_DTYPE_F32;
+        case FA_DTYPE_F32: return out_dtype == FA_DTYPE_F32;
         default: return false;
     }
 }
@@ -53,10 +39,13 @@ fa_tile default_tile(int d) {
 const Entry* find(int d, const fa_tile& t, int in_dtype, int out_dtype, int causal, int mask) {
     if (t.block_r <= 0 || t.block_r % 32 != 0) return nullptr;
     const int nw = t.block_r / 32;
-    for (const Entry& e : kTable) {
-        if (e.d == d && e.block_c == t.block_c && e.nwaves == nw && e.in_dtype == in_dtype &&
-            e.out_dtype == out_dtype && e.causal == (causal != 0) && e.mask == (mask != 0))
-            return &e;
+    for (const fa::EntryList* list : kLists) {
+        for (int i = 0; i < list->count; ++i) {
+            const Entry& e = list->entries[i];
+            if (e.d == d && e.block_c == t.block_c && e.nwaves == nw && e.in_dtype == in_dtype &&
+                e.out_dtype == out_dtype && e.causal == (causal != 0) && e.mask == (mask != 0))
+                return &e;
+        }
     }
     return nullptr;
 }

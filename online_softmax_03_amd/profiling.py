@@ -1,0 +1,142 @@
+"""HBM traffic measurement support for the attention kernel.
+
+    python -m online_softmax_03_amd.profiling copy [--mib 1024] [--reps 5]
+        a plain device-to-device copy of a known size, run under
+        `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` to calibrate the
+        counters (bytes the copy must read and write per dispatch are known).
+
+    python -m online_softmax_03_amd.profiling summarize --workload NAME \\
+        --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR [--out FILE]
+        reads the rocprofv3 counter CSVs, scales the attention kernel's
+        per-dispatch FETCH_SIZE and WRITE_SIZE by the copy kernel's
+        measured/known ratio, and writes a JSON summary stamped with a hash of
+        the kernel sources (bench.py reports the traffic only while the hash
+        still matches).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_hash() -> str:
+    """sha256 over the HIP sources and the public header (kernel identity)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [os.path.join(ROOT, "include", "fa.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"attn_fwd_kernel_{workload}_traffic.json")
+
+
+def current_traffic(workload: str):
+    """The measured traffic summary for `workload` if it matches the current
+    kernel sources, else None."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    return t if t.get("source_hash") == source_hash() else None
+
+
+def _copy(mib: int, reps: int) -> None:
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
+def _counter_rows(d: str, counter: str, name_filter: str):
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                if name_filter not in row.get("Kernel_Name", ""):
+                    continue
+                vals.append(float(row["Counter_Value"]))
+    return vals
+
+
+def _summarize(a) -> None:
+    fetch = _counter_rows(a.fetch, "FETCH_SIZE", "attn_fwd_kernel")
+    write = _counter_rows(a.write, "WRITE_SIZE", "attn_fwd_kernel")
+    cfetch = _counter_rows(a.copy_fetch, "FETCH_SIZE", a.copy_filter)
+    cwrite = _counter_rows(a.copy_write, "WRITE_SIZE", a.copy_filter)
+    if not (fetch and write and cfetch and cwrite):
+        sys.exit("missing counter rows")
+    known = a.copy_mib * 1024.0  # KiB read and written per copy dispatch
+    # the copy dispatch that moves the full buffer is the largest one
+    f_factor = known / max(cfetch)
+    w_factor = known / max(cwrite)
+    fetch_kib = sum(fetch) / len(fetch)
+    write_kib = sum(write) / len(write)
+    out = {
+        "workload": a.workload,
+        "kernel": "attn_fwd_kernel",
+        "source_hash": source_hash(),
+        "dispatches": {"fetch": len(fetch), "write": len(write)},
+        "fetch_kib_per_dispatch_raw": fetch_kib,
+        "write_kib_per_dispatch_raw": write_kib,
+        "copy_calibration": {"known_kib": known, "fetch_kib_raw": max(cfetch), "write_kib_raw": max(cwrite),
+                             "fetch_factor": f_factor, "write_factor": w_factor},
+        "hbm_bytes_per_launch": (fetch_kib * f_factor + write_kib * w_factor) * 1024.0,
+        "hbm_read_bytes_per_launch": fetch_kib * f_factor * 1024.0,
+        "hbm_write_bytes_per_launch": write_kib * w_factor * 1024.0,
+        "commands": a.commands,
+    }
+    path = a.out or traffic_file(a.workload)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=2)
+    print(json.dumps(out, indent=2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=1024)
+    c.add_argument("--reps", type=int, default=5)
+    s = sub.add_parser("summarize")
+    s.add_argument("--workload", required=True)
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--copy-fetch", required=True)
+    s.add_argument("--copy-write", required=True)
+    s.add_argument("--copy-mib", type=int, default=1024)
+    s.add_argument("--copy-filter", default="")
+    s.add_argument("--commands", nargs="*", default=[])
+    s.add_argument("--out", default=None)
+    sub.add_parser("hash")
+    a = ap.parse_args()
+    if a.cmd == "copy":
+        _copy(a.mib, a.reps)
+    elif a.cmd == "summarize":
+        _summarize(a)
+    else:
+        print(source_hash())
+
+
+if __name__ == "__main__":
+    main()

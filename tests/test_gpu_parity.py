@@ -45,6 +45,27 @@ def test_small_shapes_every_row(ident, base, over, lens):
     U.check_full(x, what=ident)
 
 
+def test_tiny_f32_workload_every_row():
+    """The fp32 workload (B=1, H=1, N=256, d=64, B_c=64) on the fp32 MFMA path:
+    O within 1e-4 and LSE within 1e-5 of the float64 oracle."""
+    w = C[TINY]
+    x = W.generate(w)
+    U.log(f"case {TINY}: tile (128, {w.block_c})")
+    O, L = U.run_gpu(x, tile=(128, w.block_c))
+    import oracle
+    Oref, Lref, fm = oracle.attention(x["q"], x["k"], x["v"], x["scale"], False)
+    eo, el = U.compare(O, L, Oref, Lref, fm, "f32", TINY)
+    U.log(f"  {TINY}: max|dO|={eo:.2e} max|dLSE|={el:.2e}")
+    assert el <= 1e-5
+
+
+@pytest.mark.parametrize("d,causal,lens", [(64, True, None), (128, False, None), (128, True, [0, 77])])
+def test_f32_path_shapes(d, causal, lens):
+    w = C[TINY].with_shape(B=2 if lens else 1, H=2, N=150, d=d, causal=causal)
+    x = W.generate(w, lens=None if lens is None else torch.tensor(lens))
+    U.check_full(x, what=f"f32 d={d} causal={causal} lens={lens}")
+
+
 WORKED = [
     # scores, values: the pages' worked examples as row 0 of an attention
     ([2.0, 4.0, 1.0, 3.0], [1.0, 1.0, 1.0, 1.0]),
