@@ -1,4 +1,4 @@
-// Attention forward with online softmax for gfx950 (MI355X): the kernel template.
+// Attention forward with online softmax for gfx950 (MI355X), bf16/fp16 inputs.
 //
 // One workgroup owns B_r = 32*NW query rows of one (batch, head); each of its
 // NW waves owns 32 of them. The workgroup walks the key/value sequence in
@@ -46,183 +46,9 @@
 // the -inf case of section 7.3, and O and LSE are stored.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "attn_common.h"
 
 namespace fa {
-
-typedef unsigned int u32;
-typedef u32 u32x2 __attribute__((ext_vector_type(2)));
-typedef u32 u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-#define FA_LDS __attribute__((address_space(3)))
-
-// Element tags.
-struct BF16 { static constexpr int kBytes = 2; };
-struct F16 { static constexpr int kBytes = 2; };
-struct F32 { static constexpr int kBytes = 4; };
-
-struct Params {
-    const void* q;
-    const void* k;
-    const void* v;
-    void* o;
-    float* lse;
-    const uint8_t* mask;  // [B][N] or nullptr
-    int B, H, N;
-    int n_qtiles;         // ceil(N / B_r)
-    int xcd_remap;        // 1: group consecutive tiles of a head on one XCD
-    float c;              // scale * log2(e)
-};
-
-constexpr float kLn2 = 0.69314718055994530942f;
-// Largest growth of a row maximum, in log2 units of the exponent, tolerated
-// before the state is rescaled: P stays below 2^8 = 256.
-constexpr float kRescaleLog2 = 8.0f;
-// Word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle.
-constexpr int kBufferFlags = 0x00020000;
-
-// ---------------------------------------------------------------- helpers
-
-template <typename T>
-__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c);
-
-template <>
-__device__ __forceinline__ f32x16 mfma32x32x16<BF16>(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-template <>
-__device__ __forceinline__ f32x16 mfma32x32x16<F16>(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// fp32 inputs: one k-pair per instruction. A: lane l holds A[l%32][l/32];
-// B: lane l holds B[l/32][l%32]; the result layout is that of the 16-bit forms.
-__device__ __forceinline__ f32x16 mfma32x32x2_f32(float a, float b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
-// Two floats rounded to nearest-even into one packed 32-bit register.
-template <typename T>
-__device__ __forceinline__ u32 pack2(float lo, float hi);
-
-template <>
-__device__ __forceinline__ u32 pack2<BF16>(float lo, float hi) {
-    bf16x2 r = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(u32, r);
-}
-
-template <>
-__device__ __forceinline__ u32 pack2<F16>(float lo, float hi) {
-    f16x2 r = {(_Float16)lo, (_Float16)hi};
-    return __builtin_bit_cast(u32, r);
-}
-
-// Value of x combined with the value in lane l^32 (one v_permlane32_swap).
-// After swap(x, x) the lower half holds (own, upper partner) and the upper
-// half (lower partner, own), so both halves combine the pair in the same order.
-__device__ __forceinline__ float pair_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float pair_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// LDS tile layout: row-major [B_c][row bytes] with the 16-byte chunk index
-// XORed by a row-dependent pattern, so that the K operand reads (16 rows x one
-// chunk per 16 lanes) and the V transpose reads (4 rows x 4 chunks per 16
-// lanes) hit distinct bank groups.
-//   CH = 8 chunks per row (bf16/fp16, d = 64):  ((row>>1)&1)<<2 | (row>>2)&3
-//   CH >= 16 (bf16/fp16 d = 128, fp32):        (row&3)<<2 | (row>>2)&3
-template <int CH>
-__device__ __forceinline__ constexpr int swz(int row) {
-    if constexpr (CH >= 16) {
-        return ((row & 3) << 2) | ((row >> 2) & 3);
-    } else {
-        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-    }
-}
-
-__device__ __forceinline__ void wait_vmcnt0() {
-    // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their no-wait maxima.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-template <typename T>
-__device__ __forceinline__ void store_row4(char* dst, const float* v4, float inv);
-
-template <>
-__device__ __forceinline__ void store_row4<F32>(char* dst, const float* v4, float inv) {
-    f32x4 r = {v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
-    *reinterpret_cast<f32x4*>(dst) = r;
-}
-
-template <>
-__device__ __forceinline__ void store_row4<BF16>(char* dst, const float* v4, float inv) {
-    u32x2 r = {pack2<BF16>(v4[0] * inv, v4[1] * inv), pack2<BF16>(v4[2] * inv, v4[3] * inv)};
-    *reinterpret_cast<u32x2*>(dst) = r;
-}
-
-template <>
-__device__ __forceinline__ void store_row4<F16>(char* dst, const float* v4, float inv) {
-    u32x2 r = {pack2<F16>(v4[0] * inv, v4[1] * inv), pack2<F16>(v4[2] * inv, v4[3] * inv)};
-    *reinterpret_cast<u32x2*>(dst) = r;
-}
-
-// Valid-key extent of one mask row over [0, n): the first and last index
-// with row[j] != 0 and the number of such indices, reduced over the whole
-// workgroup. first = INT32_MAX, last = -1 when there is none.
-template <int NT>
-__device__ __forceinline__ void mask_extent(const uint8_t* row, int n, int* first, int* last,
-                                            int* count) {
-    __shared__ int s_red[3][NT / 64];
-    int f = 0x7fffffff, l = -1, cnt = 0;
-    for (int j = threadIdx.x; j < n; j += NT) {
-        if (row[j] != 0) {
-            f = min(f, j);
-            l = max(l, j);
-            ++cnt;
-        }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        f = min(f, __shfl_xor(f, off));
-        l = max(l, __shfl_xor(l, off));
-        cnt += __shfl_xor(cnt, off);
-    }
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-        s_red[0][w] = f;
-        s_red[1][w] = l;
-        s_red[2][w] = cnt;
-    }
-    __syncthreads();
-    f = s_red[0][0];
-    l = s_red[1][0];
-    cnt = s_red[2][0];
-#pragma unroll
-    for (int i = 1; i < NT / 64; ++i) {
-        f = min(f, s_red[0][i]);
-        l = max(l, s_red[1][i]);
-        cnt += s_red[2][i];
-    }
-    *first = f;
-    *last = l;
-    *count = cnt;
-}
 
 // ---------------------------------------------------------------- kernel
 
@@ -233,8 +59,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BC % 32 == 0 && BC >= 32 && BC <= 128, "key tile");
-    constexpr bool kF32 = TI::kBytes == 4;  // fp32 inputs: fp32 MFMA, P kept in fp32
-    static_assert(!kF32 || TO::kBytes == 4, "fp32 inputs write fp32 output");
+    static_assert(TI::kBytes == 2, "16-bit inputs (fp32 inputs use attn_fwd_f32_kernel)");
     constexpr int NT = NW * 64;
     constexpr int BR = NW * 32;          // query rows per workgroup
     constexpr int NKB = BC / 32;         // 32-key blocks per tile
@@ -341,27 +166,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         }
     };
 
-    // Q^T as the B operand. 16-bit inputs: lane l holds query l%32 and
-    // d = 16*dc + 8*(l/32) .. +7 in qop[dc]. fp32 inputs: lane l holds
-    // d = (l/32)*D/2 + t in qf[t], and instruction t contracts the pair
-    // (t, D/2 + t) of d values.
-    u32x4 qop[kF32 ? 1 : NDC];
-    float qf[kF32 ? D / 2 : 1];
+    // Q^T as the B operand: lane l holds query l%32 and d = 16*dc + 8*(l/32)
+    // .. +7 in qop[dc].
+    u32x4 qop[NDC];
     {
         const int qr = min(qw0 + col, N - 1);
-        if constexpr (kF32) {
-            const char* src = qg + (size_t)qr * ROWB + hh * (ROWB / 2);
+        const char* src = qg + (size_t)qr * ROWB + hh * 16;
 #pragma unroll
-            for (int i = 0; i < D / 8; ++i) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(src + i * 16);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) qf[4 * i + j] = x[j];
-            }
-        } else {
-            const char* src = qg + (size_t)qr * ROWB + hh * 16;
-#pragma unroll
-            for (int dc = 0; dc < NDC; ++dc) qop[dc] = *reinterpret_cast<const u32x4*>(src + dc * 32);
-        }
+        for (int dc = 0; dc < NDC; ++dc) qop[dc] = *reinterpret_cast<const u32x4*>(src + dc * 32);
     }
 
     f32x16 acc[NDB];
@@ -383,8 +195,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     const int tr_r = (lane & 15) >> 2;
     const int tr_c = lane & 3;
     const int tr_dsub = (lane >> 4) & 1;
-    u32 v_off[kF32 ? 1 : NDB][2];
-    if constexpr (!kF32) {
+    u32 v_off[NDB][2];
+    {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -406,29 +218,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         f32x16 s[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-        if constexpr (kF32) {
-            // lane (col, hh) reads K[32kb + col][hh*D/2 + 4i .. +3] for 4 instructions
 #pragma unroll
-            for (int i = 0; i < D / 8; ++i) {
+        for (int dc = 0; dc < NDC; ++dc) {
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const int chunk = (hh * (D / 8) + i) ^ sw_col;
-                    const f32x4 a4 = *reinterpret_cast<const FA_LDS f32x4*>(
-                        kt + (kb * 32 + col) * ROWB + chunk * 16);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) s[kb] = mfma32x32x2_f32(a4[j], qf[4 * i + j], s[kb]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int dc = 0; dc < NDC; ++dc) {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const int chunk = (2 * dc + hh) ^ sw_col;
-                    const u32x4 a =
-                        *reinterpret_cast<const FA_LDS u32x4*>(kt + (kb * 32 + col) * ROWB + chunk * 16);
-                    s[kb] = mfma32x32x16<TI>(a, qop[dc], s[kb]);
-                }
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int chunk = (2 * dc + hh) ^ sw_col;
+                const u32x4 a =
+                    *reinterpret_cast<const FA_LDS u32x4*>(kt + (kb * 32 + col) * ROWB + chunk * 16);
+                s[kb] = mfma32x32x16<TI>(a, qop[dc], s[kb]);
             }
         }
 
@@ -485,56 +282,36 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
             }
         l_run += rs0 + rs1;
 
-        if constexpr (kF32) {
-            // ---- O^T += V_j^T P^T in fp32: register r of S^T block kb is key
-            // 32kb + 8(r/4) + 4*hh + r%4, the k = hh slot of instruction r; the
-            // A operand is V[that key][32db + col].
+        // ---- P^T as the B operand: 16-key group t of block kb is registers 8t..8t+7
+        u32x4 pb[NKB][2];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const int chunk = (8 * db + (col >> 2)) ^ swz<CH>(key);
-                        const float a = *reinterpret_cast<const FA_LDS float*>(
-                            vt + key * ROWB + chunk * 16 + (col & 3) * 4);
-                        acc[db] = mfma32x32x2_f32(a, s[kb][r], acc[db]);
-                    }
-                }
-            }
-        } else {
-            // ---- P^T as the B operand: 16-key group t of block kb is registers 8t..8t+7
-            u32x4 pb[NKB][2];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        pb[kb][t][j] = pack2<TI>(s[kb][8 * t + 2 * j], s[kb][8 * t + 2 * j + 1]);
+                for (int j = 0; j < 4; ++j)
+                    pb[kb][t][j] = pack2<TI>(s[kb][8 * t + 2 * j], s[kb][8 * t + 2 * j + 1]);
 
-            // ---- O^T += V_j^T P^T. Register j of the B operand above is key
-            // 16t + 8(j/4) + 4*hh + j%4 of the block; the A operand must hold
-            // V[that key][d = l%32] in the same slot. Two ds_read_b64_tr_b16
-            // give it: after the transpose, lane i of a 16-lane group holds
-            // V[key0 .. key0+3][dbase + i].
+        // ---- O^T += V_j^T P^T. Register j of the B operand above is key
+        // 16t + 8(j/4) + 4*hh + j%4 of the block; the A operand must hold
+        // V[that key][d = l%32] in the same slot. Two ds_read_b64_tr_b16
+        // give it: after the transpose, lane i of a 16-lane group holds
+        // V[key0 .. key0+3][dbase + i].
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int rowc = (kb * 32 + t * 16) * ROWB;
+            for (int t = 0; t < 2; ++t) {
+                const int rowc = (kb * 32 + t * 16) * ROWB;
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const i16x4 lo =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vt + rowc + v_off[db][0]));
-                        const i16x4 hi =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vt + rowc + v_off[db][1]));
-                        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-                        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-                        const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                        acc[db] = mfma32x32x16<TI>(a, pb[kb][t], acc[db]);
-                    }
+                for (int db = 0; db < NDB; ++db) {
+                    const i16x4 lo =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vt + rowc + v_off[db][0]));
+                    const i16x4 hi =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vt + rowc + v_off[db][1]));
+                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+                    const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+                    const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+                    acc[db] = mfma32x32x16<TI>(a, pb[kb][t], acc[db]);
                 }
             }
         }

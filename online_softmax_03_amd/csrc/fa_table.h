@@ -4,6 +4,7 @@
 // its entries; fa_api.hip searches them.
 #pragma once
 
+#include "attn_fwd_f32_kernel.h"
 #include "attn_fwd_kernel.h"
 #include "fa.h"
 

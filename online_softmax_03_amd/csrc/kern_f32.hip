@@ -3,9 +3,12 @@
 #include "fa_table.h"
 
 namespace fa {
+#define FA_F32_ENTRY(D, C, M) \
+    Entry{D, 64, 4, FA_DTYPE_F32, FA_DTYPE_F32, C, M, \
+          reinterpret_cast<const void*>(&attn_fwd_f32_kernel<D, 64, 4, (C) != 0, (M) != 0>)}
 static const Entry kEntries_f32[] = {
-    FA_FLAGS(64, 64, 4, F32, FA_DTYPE_F32, F32, FA_DTYPE_F32),
-    FA_FLAGS(128, 64, 4, F32, FA_DTYPE_F32, F32, FA_DTYPE_F32),
+    FA_F32_ENTRY(64, 0, 0), FA_F32_ENTRY(64, 0, 1), FA_F32_ENTRY(64, 1, 0), FA_F32_ENTRY(64, 1, 1),
+    FA_F32_ENTRY(128, 0, 0), FA_F32_ENTRY(128, 0, 1), FA_F32_ENTRY(128, 1, 0), FA_F32_ENTRY(128, 1, 1),
 };
 extern const EntryList kList_f32;
 const EntryList kList_f32 = {kEntries_f32, (int)(sizeof(kEntries_f32) / sizeof(kEntries_f32[0]))};

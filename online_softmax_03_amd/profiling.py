@@ -5,6 +5,12 @@
         `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` to calibrate the
         counters (bytes the copy must read and write per dispatch are known).
 
+    python -m online_softmax_03_amd.profiling report --workload NAME \\
+        --stats DIR --bench FILE [--traffic FILE] --command CMD --out FILE
+        writes the markdown summary of a `rocprofv3 --kernel-trace --stats`
+        run of bench.py: the attention kernel's launch statistics next to the
+        bench line measured in the same process.
+
     python -m online_softmax_03_amd.profiling summarize --workload NAME \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR [--out FILE]
         reads the rocprofv3 counter CSVs, scales the attention kernel's
@@ -112,6 +118,39 @@ def _summarize(a) -> None:
     print(json.dumps(out, indent=2))
 
 
+def _report(a) -> None:
+    stats = []
+    for f in glob.glob(os.path.join(a.stats, "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            stats.extend(csv.DictReader(fh))
+    with open(a.bench) as fh:
+        bench = json.loads([l for l in fh if l.startswith("{")][-1])
+    lines = [f"# attn_fwd_kernel on {a.workload} (MI355X)", "",
+             "Produced by (from the repository root, on one MI355X):", "", "```"]
+    lines += a.command
+    lines += ["```", "", "## rocprofv3 kernel statistics", "",
+              "| kernel | calls | average (ms) | min (ms) | max (ms) | share |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                     f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} | {float(r['Percentage']):.1f}% |")
+    rf = bench["roofline"]
+    lines += ["", "## bench.py line of the same run", "", "```json", json.dumps(bench, indent=1), "```", "",
+              f"bench.py's own per-launch HIP-event average: {rf['avg_launch_ms']:.4f} ms; "
+              f"achieved {rf['achieved']} TFLOP/s = {100 * rf['frac']:.1f}% of {rf['peak']} TFLOP/s."]
+    if a.traffic and os.path.exists(a.traffic):
+        with open(a.traffic) as fh:
+            t = json.load(fh)
+        lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE)", "",
+                  f"- read {t['hbm_read_bytes_per_launch'] / 2**20:.1f} MiB, write "
+                  f"{t['hbm_write_bytes_per_launch'] / 2**20:.1f} MiB per launch "
+                  f"(raw KiB x copy-kernel factor: fetch {t['copy_calibration']['fetch_factor']:.3f}, "
+                  f"write {t['copy_calibration']['write_factor']:.3f})",
+                  f"- source hash of the kernel sources: `{t['source_hash']}`"]
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -128,12 +167,21 @@ def main():
     s.add_argument("--copy-filter", default="")
     s.add_argument("--commands", nargs="*", default=[])
     s.add_argument("--out", default=None)
+    r = sub.add_parser("report")
+    r.add_argument("--workload", required=True)
+    r.add_argument("--stats", required=True)
+    r.add_argument("--bench", required=True)
+    r.add_argument("--traffic", default=None)
+    r.add_argument("--command", nargs="*", default=[])
+    r.add_argument("--out", required=True)
     sub.add_parser("hash")
     a = ap.parse_args()
     if a.cmd == "copy":
         _copy(a.mib, a.reps)
     elif a.cmd == "summarize":
         _summarize(a)
+    elif a.cmd == "report":
+        _report(a)
     else:
         print(source_hash())
 

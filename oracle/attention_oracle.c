@@ -115,7 +115,7 @@ int oracle_attention_rows(const float* q, const float* k, const float* v,
 #pragma omp atomic write
             err = -2;
         } else {
-#pragma omp for schedule(dynamic, 16)
+#pragma omp for schedule(dynamic, 1)
             for (long long r = 0; r < nrows; r++) {
                 long long row = rows ? rows[r] : r;
                 if (row < 0 || row >= total) {

@@ -84,6 +84,6 @@ def test_default_tile_and_supported_tiles():
     assert capi.fa_default_tile(8192, 96, BF16, BF16, 1, 0)[0] == capi.FA_ERR_HEADDIM
     assert capi.fa_default_tile(0, 128, BF16, BF16, 1, 0)[0] == capi.FA_ERR_SHAPE
     for d in (64, 128):
-        for pair in ((BF16, BF16), (BF16, F32), (F16, F16), (F16, F32)):
+        for pair in ((BF16, BF16), (BF16, F32), (F16, F16), (F16, F32), (F32, F32)):
             st, t = capi.fa_default_tile(4096, d, *pair, 0, 0)
             assert st == capi.FA_OK and capi.fa_tile_supported(d, *pair, t) == capi.FA_OK
