@@ -132,3 +132,43 @@ def test_nondefault_stream_and_repeat():
         O1, L1 = U.run_gpu(x)
     O2, L2 = U.run_gpu(x)
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+@pytest.mark.parametrize("d,dtype,causal", [(64, "f16", False), (128, "bf16", True), (64, "bf16", True),
+                                            (128, "f16", False)])
+def test_general_key_mask(d, dtype, causal):
+    """A key mask whose valid entries are not contiguous (random, plus an
+    all-padded batch and a single valid key) takes the per-key lookup path."""
+    N, B, H = 211, 4, 2
+    w = C[C5].with_shape(B=B, H=H, N=N, d=d, in_dtype=dtype, out_dtype=dtype, causal=causal,
+                         key_padding=False)
+    x = W.generate(w)
+    g = torch.Generator().manual_seed(77 + d)
+    mask = (torch.rand((B, N), generator=g) > 0.5).to(torch.uint8)
+    mask[1] = 0                      # every key padded
+    mask[2] = 0
+    mask[2, 150] = 1                 # a single valid key (causal rows < 150 see none)
+    mask[3, ::7] = 1                 # sparse, non-contiguous
+    x["mask"] = mask
+    U.check_full(x, what=f"general mask d={d} {dtype} causal={causal}")
+
+
+def _all_tiles():
+    from online_softmax_03_amd import capi
+    out = []
+    for d in (64, 128):
+        for br in (64, 128, 256, 512):
+            for bc in (32, 64, 128):
+                if capi.fa_tile_supported(d, capi.FA_DTYPE_BF16, capi.FA_DTYPE_BF16, (br, bc)) == 0:
+                    out.append((d, br, bc))
+    return out
+
+
+@pytest.mark.parametrize("d,br,bc", _all_tiles())
+@pytest.mark.parametrize("causal", [False, True])
+def test_every_tile_shape(d, br, bc, causal):
+    """Every compiled (block_r, block_c) through fa_fwd_ex, with a ragged N
+    and a padding mask on one batch."""
+    w = C[C3].with_shape(B=2, H=2, N=301, d=d, causal=causal)
+    x = W.generate(w, lens=torch.tensor([301, 97]))
+    U.check_full(x, tile=(br, bc), what=f"tile {br}x{bc} d={d} causal={causal}")
