@@ -38,6 +38,7 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -59,8 +60,13 @@ typedef enum {
     FA_ERR_SCALE = -5,     /* scale <= 0, NaN or infinite */
     FA_ERR_ALIGN = -6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_TILE = -7,      /* the requested tile configuration does not exist */
-    FA_ERR_LAUNCH = -8     /* the HIP runtime rejected the kernel launch */
+    FA_ERR_LAUNCH = -8,    /* the HIP runtime rejected the kernel launch */
+    FA_ERR_SPLITS = -9,    /* num_splits outside [1, FA_MAX_SPLITS] */
+    FA_ERR_WORKSPACE = -10 /* workspace NULL, not 16-byte aligned, or too small */
 } fa_status;
+
+/* Largest number of key-range parts fa_fwd_splitkv accepts. */
+#define FA_MAX_SPLITS 64
 
 /* Tile shape: block_r query rows per workgroup, block_c keys per K/V tile
  * (the B_r and B_c of the tiling). 0 in a field selects the default. */
@@ -106,6 +112,58 @@ int fa_default_tile(int N, int d, int in_dtype, int out_dtype, int causal, int h
 /* fa_tile_supported — FA_OK if fa_fwd_ex accepts `tile` for (d, in_dtype,
  * out_dtype), FA_ERR_TILE otherwise. Host only, no HIP call. */
 int fa_tile_supported(int d, int in_dtype, int out_dtype, const fa_tile* tile);
+
+/*
+ * Split-KV forward: the keys of every query row are cut into num_splits
+ * contiguous ranges, processed by independent workgroups, and the partial
+ * results merged afterwards. Each part runs the same tiled online-softmax loop
+ * over its own range and leaves its normalised output O_s and its LSE_s; the
+ * merge rescales the parts to their common maximum and adds them, which is the
+ * two-state merge of the online-softmax interview card (section 三, the
+ * merge equations) taken over S states at once, exact because the merge is
+ * associative and commutative ("La recurrencia del online softmax", practice
+ * problem 4). In LSE form, with M = max_s LSE_s and w_s = exp(LSE_s - M):
+ *   O = sum_s w_s O_s / sum_s w_s,   LSE = M + ln sum_s w_s.
+ * A part with no allowed key has LSE_s = -inf and weight 0; a row whose every
+ * part is empty gets O = 0 and LSE = -inf exactly, as in fa_fwd.
+ *
+ * The point is parallelism when B * H * ceil(N / block_r) workgroups cannot
+ * fill the device (small batch, few heads, short N): each part is one more
+ * workgroup. The result matches fa_fwd to rounding; only the order of the
+ * float32 additions differs.
+ */
+
+/* fa_splitkv_workspace_bytes — bytes of device workspace fa_fwd_splitkv needs:
+ * num_splits * B*H*N * (d + 1) * 4 (float32 partial outputs [S][B*H*N][d]
+ * followed by partial LSEs [S][B*H*N]). Returns 0 for invalid arguments
+ * (same rules as fa_fwd_splitkv). Host only, no HIP call. */
+size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
+
+/* fa_splitkv_num_splits — a split count for these sizes: the smallest power
+ * of two that gives at least 512 workgroups (two per compute unit), capped so
+ * that every part keeps at least four key tiles and at FA_MAX_SPLITS. Returns
+ * the count (>= 1) or a negative fa_status. Host only, no HIP call. */
+int fa_splitkv_num_splits(int B, int H, int N, int d, int in_dtype);
+
+/*
+ * fa_fwd_splitkv — attention forward with the keys split into num_splits
+ * parts, then merged. Arguments as fa_fwd, plus:
+ *   num_splits       1 .. FA_MAX_SPLITS (1 is valid: one part, then the merge)
+ *   workspace        device memory of at least
+ *                    fa_splitkv_workspace_bytes(B, H, N, d, num_splits) bytes,
+ *                    16-byte aligned, owned by the caller; its contents on
+ *                    entry do not matter and are overwritten. Two calls that
+ *                    share a workspace must be ordered (same stream, or an
+ *                    event between them): concurrent use races.
+ *   workspace_bytes  its size in bytes
+ * The tile shape is the default one for (d, in_dtype). Enqueues two kernels
+ * (the split attention pass, then the merge) on `stream`. Returns FA_OK or a
+ * negative fa_status; nothing is launched on error.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* key_padding_mask, int in_dtype, int out_dtype,
+                   int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /* fa_strerror — a static, human-readable name for a status code. */
 const char* fa_strerror(int status);

@@ -25,12 +25,17 @@ class FaError(RuntimeError):
 def attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
                   causal: bool = False, key_padding_mask: torch.Tensor | None = None,
                   out_dtype: torch.dtype | None = None, tile=None, out: torch.Tensor | None = None,
-                  lse: torch.Tensor | None = None):
+                  lse: torch.Tensor | None = None, num_splits: int | None = None,
+                  workspace: torch.Tensor | None = None):
     """O = softmax(scale * Q K^T, masked) V and LSE for [B, H, N, d] tensors.
 
     scale defaults to 1/sqrt(d). key_padding_mask: [B, N] bool/uint8 on the
     same device, True/nonzero = key valid. out_dtype defaults to q.dtype.
-    Returns (o [B, H, N, d], lse [B, H, N] float32).
+    num_splits selects the split-KV path (`fa_fwd_splitkv`): an int >= 1, or
+    0 for the library's choice (`fa_splitkv_num_splits`); it uses the default
+    tile, so `tile` must then be None. `workspace` is an optional device
+    buffer of at least `fa_splitkv_workspace_bytes` bytes (else one is
+    allocated). Returns (o [B, H, N, d], lse [B, H, N] float32).
     """
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must all be [B, H, N, d] with the same shape")
@@ -62,6 +67,25 @@ def attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: floa
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous [B, H, N] float32 tensor")
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    if num_splits is not None:
+        if tile is not None:
+            raise ValueError("the split-KV path uses the default tile")
+        if num_splits == 0:
+            num_splits = capi.fa_splitkv_num_splits(B, H, N, d, _DT[q.dtype])
+            if num_splits < 0:
+                raise FaError(num_splits)
+        need = capi.fa_splitkv_workspace_bytes(B, H, N, d, num_splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        elif workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous buffer on the same device")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        st = capi.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                 B, H, N, d, float(scale), int(bool(causal)), mask_ptr, _DT[q.dtype],
+                                 _DT[out_dtype], int(num_splits), workspace.data_ptr(), ws_bytes, stream)
+        if st != capi.FA_OK:
+            raise FaError(st)
+        return out, lse
     st = capi.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                         B, H, N, d, float(scale), int(bool(causal)), mask_ptr, _DT[q.dtype],
                         _DT[out_dtype], stream, tile)

@@ -26,9 +26,14 @@ FA_ERR_SCALE = -5
 FA_ERR_ALIGN = -6
 FA_ERR_TILE = -7
 FA_ERR_LAUNCH = -8
+FA_ERR_SPLITS = -9
+FA_ERR_WORKSPACE = -10
+
+FA_MAX_SPLITS = 64
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_default_tile", "fa_tile_supported", "fa_strerror")
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_default_tile", "fa_tile_supported", "fa_splitkv_workspace_bytes",
+           "fa_splitkv_num_splits", "fa_fwd_splitkv", "fa_strerror")
 
 
 class fa_tile(ctypes.Structure):
@@ -61,6 +66,12 @@ def library():
             lib.fa_default_tile.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.POINTER(fa_tile)]
             lib.fa_tile_supported.restype = _I
             lib.fa_tile_supported.argtypes = [_I, _I, _I, ctypes.POINTER(fa_tile)]
+            lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+            lib.fa_splitkv_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+            lib.fa_splitkv_num_splits.restype = _I
+            lib.fa_splitkv_num_splits.argtypes = [_I, _I, _I, _I, _I]
+            lib.fa_fwd_splitkv.restype = _I
+            lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:-1] + [_I, _P, ctypes.c_size_t, _P]
             lib.fa_strerror.restype = ctypes.c_char_p
             lib.fa_strerror.argtypes = [_I]
             _lib = lib
@@ -92,6 +103,20 @@ def fa_default_tile(N, d, in_dtype, out_dtype, causal, has_mask):
 
 def fa_tile_supported(d, in_dtype, out_dtype, tile) -> int:
     return library().fa_tile_supported(d, in_dtype, out_dtype, ctypes.byref(fa_tile(*tile)))
+
+
+def fa_splitkv_workspace_bytes(B, H, N, d, num_splits) -> int:
+    return int(library().fa_splitkv_workspace_bytes(B, H, N, d, num_splits))
+
+
+def fa_splitkv_num_splits(B, H, N, d, in_dtype) -> int:
+    return library().fa_splitkv_num_splits(B, H, N, d, in_dtype)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask, in_dtype, out_dtype,
+                   num_splits, workspace, workspace_bytes, stream) -> int:
+    return library().fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask,
+                                    in_dtype, out_dtype, num_splits, workspace, workspace_bytes, stream)
 
 
 def fa_strerror(status) -> str:

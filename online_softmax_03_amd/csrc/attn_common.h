@@ -37,6 +37,12 @@ struct Params {
     int n_qtiles;         // ceil(N / B_r)
     int xcd_remap;        // 1: group consecutive tiles of a head on one XCD
     float c;              // scale * log2(e)
+    // split-KV only: the key tiles of every query tile are cut into n_splits
+    // contiguous parts; part s writes its normalised partial output and its
+    // LSE to ws_o [n_splits][B*H][N][d] and ws_lse [n_splits][B*H][N].
+    int n_splits;
+    float* ws_o;
+    float* ws_lse;
 };
 
 constexpr float kLn2 = 0.69314718055994530942f;

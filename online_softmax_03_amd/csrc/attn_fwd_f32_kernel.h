@@ -16,7 +16,7 @@
 
 namespace fa {
 
-template <int D, int BC, int NW, bool CAUSAL, bool MASK>
+template <int D, int BC, int NW, bool CAUSAL, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(D == 64 || D == 128, "head dim");
@@ -43,6 +43,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(Params p) {
 
     int id = blockIdx.x;
     if (p.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
+    int split = 0;
+    if constexpr (SPLIT) {
+        split = id % p.n_splits;
+        id /= p.n_splits;
+    }
     const int bh = id / p.n_qtiles;
     const int qt = p.n_qtiles - 1 - (id - bh * p.n_qtiles);
     const int b = bh / p.H;
@@ -69,9 +74,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(Params p) {
             mask_general = count != key_hi - key_lo;
         }
     }
-    const int kv_begin = (key_lo / BC) * BC;
+    int kv_begin = (key_lo / BC) * BC;
     const int kv_end = CAUSAL ? min(key_hi, q0 + BR) : key_hi;
-    const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + BC - 1) / BC : 0;
+    int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + BC - 1) / BC : 0;
+    if constexpr (SPLIT) {
+        // this workgroup's part of the key tiles: [t0, t1) of n_tiles
+        const int per = (n_tiles + p.n_splits - 1) / p.n_splits;
+        const int t0 = min(n_tiles, split * per);
+        const int t1 = min(n_tiles, t0 + per);
+        kv_begin += t0 * BC;
+        n_tiles = t1 - t0;
+    }
 
     {
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -230,7 +243,21 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(Params p) {
     const bool dead = !(l_tot > 0.f);
     const float inv = dead ? 0.f : 1.f / l_tot;
     const float lse = dead ? -INFINITY : (m_run * c + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    if (qq < N) {
+    if (SPLIT && qq < N) {
+        // normalised partial output and LSE of this part of the keys
+        const size_t prow = ((size_t)split * p.B * p.H + bh) * N + qq;
+        char* orow = reinterpret_cast<char*>(p.ws_o + prow * D);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * db + 8 * g + 4 * hh;
+                const float v4[4] = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2],
+                                     acc[db][4 * g + 3]};
+                store_row4<F32>(orow + d0 * 4, v4, inv);
+            }
+        if (hh == 0) p.ws_lse[prow] = lse;
+    } else if (qq < N) {
         char* orow = reinterpret_cast<char*>(p.o) + (head + (size_t)qq * D) * 4;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)

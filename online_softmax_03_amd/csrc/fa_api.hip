@@ -11,6 +11,8 @@
 
 namespace fa {
 extern const EntryList kList_d128_bf16, kList_d128_f16, kList_d64_bf16, kList_d64_f16, kList_f32;
+extern const MergeEntry* const kMerge;
+extern const int kMergeCount;
 }
 
 namespace {
@@ -40,18 +42,69 @@ fa_tile default_tile(int d, int in_dtype) {
     return d == 128 ? fa_tile{128, 32} : fa_tile{256, 64};
 }
 
-const Entry* find(int d, const fa_tile& t, int in_dtype, int out_dtype, int causal, int mask) {
+// The split-KV kernels write fp32 partials whatever the final output dtype,
+// so for them the output dtype is not part of the match.
+const Entry* find(int d, const fa_tile& t, int in_dtype, int out_dtype, int causal, int mask,
+                  int split = 0) {
     if (t.block_r <= 0 || t.block_r % 32 != 0) return nullptr;
     const int nw = t.block_r / 32;
     for (const fa::EntryList* list : kLists) {
         for (int i = 0; i < list->count; ++i) {
             const Entry& e = list->entries[i];
             if (e.d == d && e.block_c == t.block_c && e.nwaves == nw && e.in_dtype == in_dtype &&
-                e.out_dtype == out_dtype && e.causal == (causal != 0) && e.mask == (mask != 0))
+                (split || e.out_dtype == out_dtype) && e.causal == (causal != 0) && e.mask == (mask != 0) &&
+                e.split == split)
                 return &e;
         }
     }
     return nullptr;
+}
+
+const fa::MergeEntry* find_merge(int d, int out_dtype) {
+    for (int i = 0; i < fa::kMergeCount; ++i)
+        if (fa::kMerge[i].d == d && fa::kMerge[i].out_dtype == out_dtype) return &fa::kMerge[i];
+    return nullptr;
+}
+
+// Workspace of the split-KV path: fp32 partial outputs [S][B*H*N][d], then
+// their LSEs [S][B*H*N]. 0 if the sizes are out of range.
+size_t splitkv_bytes(int B, int H, int N, int d, int S) {
+    if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128) || S < 1 || S > FA_MAX_SPLITS) return 0;
+    const long long rows = (long long)B * H * N;
+    if (rows > (1LL << 40)) return 0;
+    return (size_t)S * (size_t)rows * (size_t)(d + 1) * sizeof(float);
+}
+
+// Shared argument checks of fa_fwd_ex and fa_fwd_splitkv.
+int check_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                 int d, float scale, int in_dtype, int out_dtype) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (!dtype_pair_ok(in_dtype, out_dtype)) return FA_ERR_DTYPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+void fill_params(fa::Params& prm, const void* q, const void* k, const void* v, void* o, float* lse,
+                 const uint8_t* mask, int B, int H, int N, float scale, long long n_qtiles, long long grid) {
+    prm.q = q;
+    prm.k = k;
+    prm.v = v;
+    prm.o = o;
+    prm.lse = lse;
+    prm.mask = mask;
+    prm.B = B;
+    prm.H = H;
+    prm.N = N;
+    prm.n_qtiles = (int)n_qtiles;
+    prm.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    prm.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+    prm.n_splits = 1;
+    prm.ws_o = nullptr;
+    prm.ws_lse = nullptr;
 }
 
 fa_tile resolve(int d, int in_dtype, const fa_tile* tile) {
@@ -78,6 +131,8 @@ const char* fa_strerror(int status) {
         case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
         case FA_ERR_TILE: return "no kernel for the requested tile shape";
         case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_SPLITS: return "num_splits must be in [1, FA_MAX_SPLITS]";
+        case FA_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned, or too small";
         default: return "unknown status";
     }
 }
@@ -101,13 +156,8 @@ int fa_default_tile(int N, int d, int in_dtype, int out_dtype, int causal, int h
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
               int d, float scale, int causal, const uint8_t* key_padding_mask, int in_dtype,
               int out_dtype, void* stream, const fa_tile* tile) {
-    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
-    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-    if (!dtype_pair_ok(in_dtype, out_dtype)) return FA_ERR_DTYPE;
-    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
-        return FA_ERR_ALIGN;
+    const int st = check_common(q, k, v, o, lse, B, H, N, d, scale, in_dtype, out_dtype);
+    if (st != FA_OK) return st;
     const fa_tile t = resolve(d, in_dtype, tile);
     const Entry* e = find(d, t, in_dtype, out_dtype, causal, key_padding_mask != nullptr);
     if (!e) return FA_ERR_TILE;
@@ -119,18 +169,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
     if (rows > (1LL << 40) || (long long)N * d * 4 > INT32_MAX || grid > INT32_MAX) return FA_ERR_SHAPE;
 
     fa::Params prm;
-    prm.q = q;
-    prm.k = k;
-    prm.v = v;
-    prm.o = o;
-    prm.lse = lse;
-    prm.mask = key_padding_mask;
-    prm.B = B;
-    prm.H = H;
-    prm.N = N;
-    prm.n_qtiles = (int)n_qtiles;
-    prm.xcd_remap = (grid % 8 == 0) ? 1 : 0;
-    prm.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+    fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, n_qtiles, grid);
     void* args[] = {&prm};
     const hipError_t err = hipLaunchKernel(e->fn, dim3((unsigned)grid), dim3(e->nwaves * 64), args, 0,
                                            reinterpret_cast<hipStream_t>(stream));
@@ -142,6 +181,68 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            void* stream) {
     return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask, in_dtype, out_dtype,
                      stream, nullptr);
+}
+
+size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
+    return splitkv_bytes(B, H, N, d, num_splits);
+}
+
+int fa_splitkv_num_splits(int B, int H, int N, int d, int in_dtype) {
+    if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16 && in_dtype != FA_DTYPE_F16) return FA_ERR_DTYPE;
+    const fa_tile t = default_tile(d, in_dtype);
+    const long long grid = (long long)B * H * (((long long)N + t.block_r - 1) / t.block_r);
+    const long long key_tiles = ((long long)N + t.block_c - 1) / t.block_c;
+    // Enough workgroups for two per compute unit (256 CUs), keeping at least
+    // four key tiles per part.
+    long long s = 1;
+    while (s < FA_MAX_SPLITS && grid * s < 512 && key_tiles / (2 * s) >= 4) s *= 2;
+    return (int)s;
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                   int d, float scale, int causal, const uint8_t* key_padding_mask, int in_dtype,
+                   int out_dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = check_common(q, k, v, o, lse, B, H, N, d, scale, in_dtype, out_dtype);
+    if (st != FA_OK) return st;
+    if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+    const size_t need = splitkv_bytes(B, H, N, d, num_splits);
+    if (need == 0) return FA_ERR_SHAPE;
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    const fa_tile t = default_tile(d, in_dtype);
+    const Entry* e = find(d, t, in_dtype, out_dtype, causal, key_padding_mask != nullptr, 1);
+    const fa::MergeEntry* me = find_merge(d, out_dtype);
+    if (!e || !me) return FA_ERR_TILE;
+    const long long rows = (long long)B * H * N;
+    const long long n_qtiles = ((long long)N + t.block_r - 1) / t.block_r;
+    const long long grid = (long long)B * H * n_qtiles * num_splits;
+    const long long rows_per_block = 256 / (d / 4);
+    const long long merge_grid = (rows + rows_per_block - 1) / rows_per_block;
+    if ((long long)N * d * 4 > INT32_MAX || grid > INT32_MAX || merge_grid > INT32_MAX) return FA_ERR_SHAPE;
+
+    float* ws_o = static_cast<float*>(workspace);
+    float* ws_lse = ws_o + (size_t)num_splits * (size_t)rows * (size_t)d;
+    fa::Params prm;
+    fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, n_qtiles, grid);
+    prm.n_splits = num_splits;
+    prm.ws_o = ws_o;
+    prm.ws_lse = ws_lse;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    void* args[] = {&prm};
+    if (hipLaunchKernel(e->fn, dim3((unsigned)grid), dim3(e->nwaves * 64), args, 0, s) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    fa::MergeParams mp;
+    mp.ws_o = ws_o;
+    mp.ws_lse = ws_lse;
+    mp.o = o;
+    mp.lse = lse;
+    mp.rows = rows;
+    mp.n_splits = num_splits;
+    void* margs[] = {&mp};
+    if (hipLaunchKernel(me->fn, dim3((unsigned)merge_grid), dim3(256), margs, 0, s) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
 }
 
 }  // extern "C"

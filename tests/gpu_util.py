@@ -23,9 +23,10 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_gpu(x: dict, tile=None, canary=True):
-    """Runs the HIP path on inputs `x` (from workloads.generate). Returns
-    (O float64 numpy, LSE float64 numpy) on the CPU."""
+def run_gpu(x: dict, tile=None, canary=True, num_splits=None):
+    """Runs the HIP path on inputs `x` (from workloads.generate); with
+    `num_splits` the split-KV entry point, on a workspace pre-filled with NaN
+    bytes. Returns (O float64 numpy, LSE float64 numpy) on the CPU."""
     dev = torch.device("cuda:0")
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     mask = None if x["mask"] is None else x["mask"].to(dev)
@@ -35,8 +36,14 @@ def run_gpu(x: dict, tile=None, canary=True):
     if canary:
         o.fill_(float("nan"))
         lse.fill_(float("nan"))
+    ws = None
+    if num_splits is not None:
+        B, H, N, d = q.shape
+        s = num_splits or A.capi.fa_splitkv_num_splits(B, H, N, d, A._DT[q.dtype])
+        ws = torch.full((A.capi.fa_splitkv_workspace_bytes(B, H, N, d, s),), 0xFF, dtype=torch.uint8, device=dev)
+        num_splits = s
     A.attention_fwd(q, k, v, scale=x["scale"], causal=x["causal"], key_padding_mask=mask,
-                    out_dtype=out_dt, tile=tile, out=o, lse=lse)
+                    out_dtype=out_dt, tile=tile, out=o, lse=lse, num_splits=num_splits, workspace=ws)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -56,8 +63,8 @@ def compare(O, L, Oref, Lref, fm, in_dtype, what=""):
     return errO, errL
 
 
-def check_full(x: dict, tile=None, what=""):
-    O, L = run_gpu(x, tile)
+def check_full(x: dict, tile=None, what="", num_splits=None):
+    O, L = run_gpu(x, tile, num_splits=num_splits)
     Oref, Lref, fm = oracle.attention(x["q"], x["k"], x["v"], x["scale"], x["causal"], x["mask"])
     e = compare(O, L, Oref, Lref, fm, x["in_dtype"], what)
     log(f"  {what}: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e} masked_rows={int(fm.sum())}")
@@ -75,10 +82,10 @@ def sample_rows(B, H, N, n, seed, causal):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def check_sampled(x: dict, rows, tile=None, what=""):
+def check_sampled(x: dict, rows, tile=None, what="", num_splits=None):
     """Full-size run on the GPU; the oracle computes only `rows`, one head at a
     time (the oracle reads just that head's Q, K, V)."""
-    O, L = run_gpu(x, tile)
+    O, L = run_gpu(x, tile, num_splits=num_splits)
     B, H, N, d = x["q"].shape
     Of, Lf = O.reshape(-1, d), L.reshape(-1)
     errs = []

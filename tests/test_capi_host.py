@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_names_every_status():
-    names = {s: capi.fa_strerror(s) for s in range(-8, 1)}
+    names = {s: capi.fa_strerror(s) for s in range(-10, 1)}
     assert names[0] == "ok"
     assert len(set(names.values())) == len(names)
     assert capi.fa_strerror(-99) == "unknown status"
@@ -87,3 +87,47 @@ def test_default_tile_and_supported_tiles():
         for pair in ((BF16, BF16), (BF16, F32), (F16, F16), (F16, F32), (F32, F32)):
             st, t = capi.fa_default_tile(4096, d, *pair, 0, 0)
             assert st == capi.FA_OK and capi.fa_tile_supported(d, *pair, t) == capi.FA_OK
+
+
+def test_splitkv_workspace_bytes():
+    # [S][B*H*N][d] float32 partial outputs, then [S][B*H*N] float32 LSEs
+    assert capi.fa_splitkv_workspace_bytes(2, 3, 100, 64, 4) == 4 * 2 * 3 * 100 * (64 + 1) * 4
+    assert capi.fa_splitkv_workspace_bytes(1, 1, 1, 128, 1) == (128 + 1) * 4
+    for bad in ((0, 1, 8, 64, 2), (1, 1, 0, 64, 2), (1, 1, 8, 96, 2), (1, 1, 8, 64, 0),
+                (1, 1, 8, 64, capi.FA_MAX_SPLITS + 1), (1 << 16, 1 << 16, 1 << 16, 64, 1)):
+        assert capi.fa_splitkv_workspace_bytes(*bad) == 0, bad
+
+
+def test_splitkv_num_splits_heuristic():
+    # a full grid needs no split; a small one splits until ~512 workgroups,
+    # keeping at least four key tiles per part
+    assert capi.fa_splitkv_num_splits(2, 32, 8192, 128, BF16) == 1
+    s = capi.fa_splitkv_num_splits(1, 2, 4096, 128, BF16)
+    assert s > 1 and s & (s - 1) == 0 and s <= capi.FA_MAX_SPLITS
+    assert 1 * 2 * (4096 // 128) * s >= 512 or (4096 // 32) // (2 * s) < 4
+    assert capi.fa_splitkv_num_splits(1, 1, 64, 128, BF16) == 1  # too few key tiles to split
+    assert capi.fa_splitkv_num_splits(1, 1, 0, 128, BF16) == capi.FA_ERR_SHAPE
+    assert capi.fa_splitkv_num_splits(1, 1, 64, 80, BF16) == capi.FA_ERR_HEADDIM
+    assert capi.fa_splitkv_num_splits(1, 1, 64, 64, 9) == capi.FA_ERR_DTYPE
+
+
+def _split(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=128, scale=0.125, causal=0,
+             key_padding_mask=None, in_dtype=BF16, out_dtype=BF16, num_splits=2, workspace=P,
+             workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return capi.fa_fwd_splitkv(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), capi.FA_ERR_NULL), (dict(lse=None), capi.FA_ERR_NULL),
+    (dict(N=0), capi.FA_ERR_SHAPE), (dict(d=32), capi.FA_ERR_HEADDIM),
+    (dict(out_dtype=F16), capi.FA_ERR_DTYPE), (dict(scale=float("nan")), capi.FA_ERR_SCALE),
+    (dict(v=P + 4), capi.FA_ERR_ALIGN),
+    (dict(num_splits=0), capi.FA_ERR_SPLITS), (dict(num_splits=capi.FA_MAX_SPLITS + 1), capi.FA_ERR_SPLITS),
+    (dict(workspace=None), capi.FA_ERR_WORKSPACE), (dict(workspace=P + 8), capi.FA_ERR_WORKSPACE),
+    (dict(workspace_bytes=2 * 128 * 129 * 4 - 1), capi.FA_ERR_WORKSPACE),
+    (dict(B=1 << 16, H=1 << 16, N=1 << 16), capi.FA_ERR_SHAPE),
+])
+def test_splitkv_invalid_arguments_rejected_on_host(kw, status):
+    assert _split(**kw) == status
