@@ -1,11 +1,16 @@
 """Benchmark of the attention forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--tile R,C]
-                    [--no-cpu-baseline] [--gpus 1]
+                    [--shape B,H,N] [--num-splits S] [--no-cpu-baseline] [--gpus 1]
 
 A step is one attention forward (one fa_fwd call) over the whole workload,
 inputs already resident in HBM. Prints ONE JSON line. The default workload is
 bf16, causal, d=128, N=8192, B=2, H=32.
+
+--shape replaces the workload's (B, H, N) (the workload is then reported as
+NAME@BxHxN). --num-splits S times the split-KV entry point instead (S = 0:
+the library's choice); a step is then its two launches, attention and merge,
+and the per-launch time in `roofline` covers both.
 """
 from __future__ import annotations
 
@@ -32,6 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--tile", default=None, help="block_r,block_c")
+    ap.add_argument("--shape", default=None, help="B,H,N")
+    ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -101,6 +108,9 @@ def main():
     from online_softmax_03_amd import workloads as W
 
     w = W.BY_NAME[args.workload]
+    if args.shape:
+        B, H, N = (int(t) for t in args.shape.split(","))
+        w = w.with_shape(B=B, H=H, N=N, name=f"{w.name}@{B}x{H}x{N}")
     x = W.generate(w)
     dev = torch.device("cuda:0")
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
@@ -115,10 +125,22 @@ def main():
         assert st == 0
 
     stream = torch.cuda.current_stream(dev)
+    splits, ws = args.num_splits, None
+    if splits is not None:
+        if args.tile:
+            sys.exit("--num-splits uses the default tile; drop --tile")
+        if splits == 0:
+            splits = capi.fa_splitkv_num_splits(w.B, w.H, w.N, w.d, A._DT[q.dtype])
+        ws = torch.empty(capi.fa_splitkv_workspace_bytes(w.B, w.H, w.N, w.d, splits), dtype=torch.uint8,
+                         device=dev)
 
     def step():
-        A.attention_fwd(q, k, v, scale=w.scale, causal=w.causal, key_padding_mask=mask,
-                        out_dtype=out_dt, tile=tile, out=o, lse=lse)
+        if splits is None:
+            A.attention_fwd(q, k, v, scale=w.scale, causal=w.causal, key_padding_mask=mask,
+                            out_dtype=out_dt, tile=tile, out=o, lse=lse)
+        else:
+            A.attention_fwd(q, k, v, scale=w.scale, causal=w.causal, key_padding_mask=mask,
+                            out_dtype=out_dt, out=o, lse=lse, num_splits=splits, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -142,7 +164,7 @@ def main():
     value = flops * args.steps / wall / 1e12
     achieved = flops / avg_launch_s / 1e12
     peak = PEAK_TFLOPS[w.in_dtype]
-    hbm_bytes, hbm_detail = traffic(w.name)
+    hbm_bytes, hbm_detail = traffic(w.name) if splits is None else (None, None)
     result = {
         "metric": "attention fwd TFLOP/s and % of MFMA bf16 peak (causal, d=128, N=8192)",
         "value": round(value, 2),
@@ -158,7 +180,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "key_padding": w.key_padding, "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
-                   "block_r": tile[0], "block_c": tile[1], "flops_per_step": flops},
+                   "block_r": tile[0], "block_c": tile[1], "num_splits": splits, "flops_per_step": flops},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": hbm_bytes, "traffic_detail": hbm_detail,
