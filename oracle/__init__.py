@@ -5,9 +5,13 @@ baseline import this package; the product path (the HIP library and its
 Python binding) never does, and the two share no code.
 
 - `attention(...)`: float64 three-pass safe-softmax attention (plain C).
+- `softmax_rows(x)`: float64 three-pass safe softmax of every row of a matrix
+  (the standalone row-softmax operation).
 - `softmax_ref.safe_softmax`, `softmax_ref.online_softmax`,
-  `softmax_ref.online_attention`, `softmax_ref.merge_states`: score-level and
-  blocked references used to pin the three-pass oracle (and vice versa).
+  `softmax_ref.online_two_pass`, `softmax_ref.online_attention`,
+  `softmax_ref.merge_states`: score-level and blocked references used to pin
+  the three-pass oracles (and vice versa).
 """
 from .attention import attention, build, load, max_threads  # noqa: F401
+from .softmax_rows import softmax_rows  # noqa: F401
 from . import softmax_ref  # noqa: F401

@@ -35,6 +35,33 @@ def safe_softmax(s):
     return p, float(m), l, float(m + np.log(l))
 
 
+def online_two_pass(x):
+    """The online softmax in two passes over a 1-D vector, element by element.
+
+    Follows "Online Softmax 算法详解" section 2.2: pass 1 fuses the maximum
+    and the normaliser (for each element, m_new = max(m, x_i), then
+    l = exp(m - m_new) * l + exp(x_i - m_new), m = m_new), pass 2 writes
+    exp(x_i - m) / l. The -inf guard of section 7.1 of that page replaces the
+    reference point by 0 while everything seen is -inf. Pure Python over
+    float64 scalars, for small inputs only.
+
+    Returns (y list, m, l, lse).
+    """
+    import math
+
+    m, l = -math.inf, 0.0
+    for xi in x:                                   # pass 1
+        xi = float(xi)
+        m_new = max(m, xi)
+        ref = 0.0 if m_new == -math.inf else m_new
+        l = (math.exp(m - ref) if m != -math.inf else 0.0) * l + math.exp(xi - ref)
+        m = m_new
+    if m == -math.inf:
+        return [0.0] * len(x), m, 0.0, -math.inf
+    y = [math.exp(float(xi) - m) / l for xi in x]  # pass 2
+    return y, m, l, m + math.log(l)
+
+
 def online_softmax(blocks, v_blocks=None, dtype=np.float64):
     """The online recurrence over a sequence of score blocks.
 
