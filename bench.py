@@ -7,7 +7,11 @@ A step is one attention forward (one fa_fwd call) over the whole workload,
 inputs already resident in HBM. Prints ONE JSON line. The default workload is
 bf16, causal, d=128, N=8192, B=2, H=32.
 
---shape replaces the workload's (B, H, N) (the workload is then reported as
+--workload sm_* times the standalone row softmax instead (one fa_softmax_fwd
+call per step; HBM-bound, reported in GB/s of algorithmic traffic: x read
+once, y and LSE written once).
+
+--shape replaces the workload's (B, H, N), or (rows, cols) for sm_* workloads (the workload is then reported as
 NAME@BxHxN). --num-splits S times the split-KV entry point instead (S = 0:
 the library's choice); a step is then its two launches, attention and merge,
 and the per-launch time in `roofline` covers both.
@@ -26,6 +30,8 @@ if ROOT not in sys.path:
 
 # MI355X dense MFMA peak for bf16/fp16: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+# MI355X HBM3E peak bandwidth.
+PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_causal_n8192_d128"
 KERNEL_PREFIX = "attn_fwd_kernel"
 
@@ -80,18 +86,115 @@ def cpu_baseline(w, x, target_s):
                       f"oracle, nominal 4*d*(allowed keys) FLOP per row, {dt:.1f} s"}
 
 
-def traffic(workload):
+def traffic(workload, kernel=KERNEL_PREFIX):
     """(HBM bytes per launch, detail) from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary, when it was taken on the current kernel sources; else
     (None, None)."""
     from online_softmax_03_amd import profiling
-    t = profiling.current_traffic(workload)
+    t = profiling.current_traffic(workload, kernel)
     if t is None:
         return None, None
     return round(t["hbm_bytes_per_launch"]), {
         "read_bytes": round(t["hbm_read_bytes_per_launch"]),
         "write_bytes": round(t["hbm_write_bytes_per_launch"]),
-        "source": os.path.relpath(profiling.traffic_file(workload), ROOT)}
+        "source": os.path.relpath(profiling.traffic_file(workload, kernel), ROOT)}
+
+
+def timed_steps(step, stream, steps, warmup):
+    """Runs `warmup` untimed steps, then `steps` timed ones with a HIP event
+    pair around each on `stream`. Returns (wall seconds, per-launch ms list)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def softmax_cpu_baseline(w, x, target_s):
+    """Times the float64 row-softmax oracle on a bounded random sample of rows
+    of the same workload; reports GB/s of the workload's algorithmic bytes."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(123)
+    xf = x.float().numpy()
+    per_row = w.algorithmic_bytes() / w.rows
+
+    def run(n):
+        rows = np.sort(rng.choice(w.rows, size=n, replace=False))
+        t0 = time.perf_counter()
+        for i in range(0, n, 64):
+            oracle.softmax_rows(xf[rows[i:i + 64]])
+        return time.perf_counter() - t0
+
+    run(8)
+    dt = run(64)
+    n = int(min(w.rows, max(64, 64 * target_s / max(dt, 1e-3))))
+    dt = run(n)
+    return {"value": round(per_row * n / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} rows of {w.name} drawn uniformly at random (seed 123), float64 numpy three-pass "
+                      f"oracle in one thread, bytes counted as for the GPU, {dt:.1f} s"}
+
+
+def bench_softmax(args):
+    import torch
+    from online_softmax_03_amd import softmax as S
+    from online_softmax_03_amd import workloads as W
+
+    w = W.SOFTMAX_BY_NAME[args.workload]
+    if args.shape:
+        rows, cols = (int(t) for t in args.shape.split(","))
+        w = w.with_shape(rows=rows, cols=cols, name=f"{w.name}@{rows}x{cols}")
+    x = W.generate_softmax(w)
+    dev = torch.device("cuda:0")
+    xd = x.to(dev)
+    y = torch.empty(x.shape, dtype=W.DTYPES[w.out_dtype], device=dev)
+    lse = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        S.softmax_rows(xd, out_dtype=y.dtype, out=y, lse=lse)
+
+    wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup)
+    avg_s = sum(launch_ms) / len(launch_ms) / 1e3
+    nbytes = w.algorithmic_bytes()
+    kernel = "softmax_resident_kernel" if (w.cols % (4 if w.in_dtype == "f32" else 8) == 0 and
+                                           w.cols <= (32768 if w.in_dtype == "f32" else 65536)) \
+        else "softmax_stream_kernel"
+    hbm_bytes, hbm_detail = traffic(w.name, kernel)
+    result = {
+        "metric": "row softmax HBM GB/s (algorithmic bytes: x read once, y and LSE written once)",
+        "value": round(nbytes * args.steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.in_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "in_dtype": w.in_dtype,
+                   "out_dtype": w.out_dtype, "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / avg_s / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": hbm_bytes, "traffic_detail": hbm_detail, "kernel": kernel,
+                     "avg_launch_ms": round(avg_s * 1e3, 4),
+                     "min_launch_ms": round(min(launch_ms), 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = softmax_cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
 
 
 def main():
@@ -101,6 +204,9 @@ def main():
               "(the path shards over (batch, head) with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload.startswith("sm_"):
+        return bench_softmax(args)
 
     import torch
     from online_softmax_03_amd import attention as A
@@ -142,22 +248,8 @@ def main():
             A.attention_fwd(q, k, v, scale=w.scale, causal=w.causal, key_padding_mask=mask,
                             out_dtype=out_dt, out=o, lse=lse, num_splits=splits, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     # per-launch HIP events on the stream the kernel is launched on
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
 
     flops = w.nominal_flops()
@@ -184,7 +276,8 @@ def main():
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": hbm_bytes, "traffic_detail": hbm_detail,
-                     "kernel": KERNEL_PREFIX, "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
+                     "kernel": KERNEL_PREFIX, "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                     "min_launch_ms": round(min(launch_ms), 4)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

@@ -165,6 +165,36 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    const uint8_t* key_padding_mask, int in_dtype, int out_dtype,
                    int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_softmax_fwd — softmax of every row of a matrix, with the online
+ * normaliser.
+ *
+ * For each row x (length cols): m = max_i x_i, l = sum_i exp(x_i - m),
+ *   y_i = exp(x_i - m) / l,   lse = m + ln l.
+ * This is the two-pass online softmax of "Online Softmax 算法详解" section 2.2:
+ * pass 1 produces m and l together with the incremental update (a larger
+ * maximum rescales the running sum by exp(m_old - m_new)), pass 2 writes y.
+ * Partial states of parts of a row combine with the merge of the
+ * online-softmax interview card (section 三). Entries equal to -inf are
+ * masked (y = 0 there); a row with no finite entry gets y = 0 and lse = -inf
+ * exactly. Arithmetic is float32 (exp as exp2 with log2(e) folded in).
+ *
+ *   x     [rows][cols] in_dtype, device, 16-byte aligned, row-major
+ *   y     [rows][cols] out_dtype, device, 16-byte aligned (written). y may be
+ *         x itself when in_dtype == out_dtype; any other overlap is undefined.
+ *   lse   [rows] float32, device (written; natural log), or NULL
+ *   rows  1 .. 2^31 - 1;  cols >= 1;  rows * cols <= 2^40
+ *   in_dtype, out_dtype  as fa_fwd: (BF16, BF16), (BF16, F32), (F16, F16),
+ *         (F16, F32), (F32, F32)
+ *   stream  hipStream_t, or NULL
+ * A row of at most 65536 (16-bit) or 32768 (fp32) elements whose length is a
+ * multiple of 8 (16-bit) or 4 (fp32) elements is held in registers: x is read
+ * from memory once. Other rows are streamed twice (one workgroup per row).
+ * Returns FA_OK or a negative fa_status; nothing is launched on error.
+ */
+int fa_softmax_fwd(const void* x, void* y, float* lse, long long rows, int cols,
+                   int in_dtype, int out_dtype, void* stream);
+
 /* fa_strerror — a static, human-readable name for a status code. */
 const char* fa_strerror(int status);
 

@@ -1,0 +1,308 @@
+// Row softmax with the online normaliser on gfx950 (MI355X).
+//
+// For every row x of a [rows][cols] matrix: y = exp(x - m) / l with
+// m = max x and l = sum exp(x - m), plus LSE = m + ln l. The method is the
+// two-pass online softmax of "Online Softmax 算法详解" section 2.2: the first
+// pass produces m and l together by the incremental update (a new maximum
+// rescales the running sum by exp(m_old - m_new)), the second pass writes
+// the normalised values. Partial (m, l) states of different parts of a row
+// combine with the merge of the online-softmax interview card (section 三):
+// m = max(m1, m2), l = l1 e^(m1 - m) + l2 e^(m2 - m). exp is evaluated as
+// exp2 of (x - m) * log2(e); the subtraction comes first so that large inputs
+// close to the maximum keep their precision. Entries equal to -inf are
+// masked; a row with no finite entry gets y = 0 and LSE = -inf exactly (the
+// guards of "Online Softmax 算法详解" sections 7.1-7.3).
+//
+// Two kernels, both HBM-bound:
+//   softmax_resident_kernel: the row stays in registers, so x is read from
+//     HBM once and y written once. Each thread takes a slice of the row
+//     (16-byte vectors, coalesced across the threads of the row), computes
+//     the slice's maximum and the sum of its exponentials (kept in
+//     registers), the slices' (m, l) states are merged across the lanes of a
+//     wave (butterfly, bitwise identical in every lane because the merge is
+//     commutative in IEEE arithmetic) and across the waves of the row (LDS,
+//     in a fixed order), and each thread rescales its exponentials by
+//     e^(m_slice - m) / l.
+//   softmax_stream_kernel: rows too long for registers, or whose length is
+//     not a whole number of 16-byte vectors. Pass 1 streams the row and keeps
+//     a running (m, l) per thread, updated per vector; pass 2 streams it again
+//     and writes y. One workgroup per row.
+#pragma once
+
+#include "attn_common.h"
+#include "softmax_table.h"
+
+namespace fa {
+
+constexpr float kSmLog2e = 1.44269504088896340736f;
+
+// ---------------------------------------------------------------- element I/O
+
+// One 16-byte input vector as floats: 8 (bf16, fp16) or 4 (fp32) values.
+template <typename T>
+struct VecIn;
+
+template <>
+struct VecIn<BF16> {
+    static constexpr int kN = 8;
+    __device__ static void load(const char* p, float* v) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(u[i] << 16);
+            v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+    __device__ static float load1(const char* p) {
+        return __uint_as_float((u32)(*reinterpret_cast<const unsigned short*>(p)) << 16);
+    }
+};
+
+template <>
+struct VecIn<F16> {
+    static constexpr int kN = 8;
+    __device__ static void load(const char* p, float* v) {
+        const f16x8 h = *reinterpret_cast<const f16x8*>(p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+    }
+    __device__ static float load1(const char* p) { return (float)*reinterpret_cast<const _Float16*>(p); }
+};
+
+template <>
+struct VecIn<F32> {
+    static constexpr int kN = 4;
+    __device__ static void load(const char* p, float* v) {
+        const f32x4 f = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = f[i];
+    }
+    __device__ static float load1(const char* p) { return *reinterpret_cast<const float*>(p); }
+};
+
+// N values times s, rounded to the output dtype and stored at p (N * size
+// bytes, 16-byte aligned when N * size is a multiple of 16).
+template <typename T, int N>
+__device__ __forceinline__ void store_scaled(char* p, const float* v, float s) {
+    if constexpr (T::kBytes == 4) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const f32x4 r = {v[i] * s, v[i + 1] * s, v[i + 2] * s, v[i + 3] * s};
+            *reinterpret_cast<f32x4*>(p + 4 * i) = r;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 8) {
+            const u32x4 r = {pack2<T>(v[i] * s, v[i + 1] * s), pack2<T>(v[i + 2] * s, v[i + 3] * s),
+                             pack2<T>(v[i + 4] * s, v[i + 5] * s), pack2<T>(v[i + 6] * s, v[i + 7] * s)};
+            *reinterpret_cast<u32x4*>(p + 2 * i) = r;
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store1(char* p, float v) {
+    if constexpr (T::kBytes == 4) {
+        *reinterpret_cast<float*>(p) = v;
+    } else {
+        const u32 w = pack2<T>(v, 0.f);
+        *reinterpret_cast<unsigned short*>(p) = (unsigned short)(w & 0xffffu);
+    }
+}
+
+// ---------------------------------------------------------------- (m, l) states
+
+// exp2 of the exponent offset that brings a state with maximum `m` to the
+// reference `ref` (log2(e) folded in); 0 for an empty state.
+__device__ __forceinline__ float sm_rescale(float m, float ref) {
+    return __builtin_amdgcn_exp2f((m - ref) * kSmLog2e);
+}
+
+// Merge of two partial states (m1, l1) and (m2, l2), in place into (m, l).
+// Symmetric in its two arguments, so every lane of a butterfly ends with the
+// same bits.
+__device__ __forceinline__ void sm_merge(float& m, float& l, float m2, float l2) {
+    const float mm = fmaxf(m, m2);
+    const float ref = (mm == -INFINITY) ? 0.f : mm;
+    l = l * sm_rescale(m, ref) + l2 * sm_rescale(m2, ref);
+    m = mm;
+}
+
+// Merge over the 64 lanes of a wave; every lane ends with the wave's state.
+__device__ __forceinline__ void sm_wave_merge(float& m, float& l) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float m2 = __shfl_xor(m, off, 64);
+        const float l2 = __shfl_xor(l, off, 64);
+        sm_merge(m, l, m2, l2);
+    }
+}
+
+// ---------------------------------------------------------------- resident rows
+
+// WPR waves per row, RPB rows per workgroup, VPT 16-byte input vectors per
+// thread: rows of up to WPR * 64 * VPT vectors. cols must be a multiple of
+// the vector width; rows start 16-byte aligned.
+template <typename TI, typename TO, int WPR, int RPB, int VPT>
+__global__ __launch_bounds__(WPR * RPB * 64) void softmax_resident_kernel(SoftmaxParams sp) {
+    constexpr int E = VecIn<TI>::kN;
+    constexpr int RT = WPR * 64;  // threads per row
+    __shared__ float s_m[RPB][WPR], s_l[RPB][WPR];
+
+    const int tid = threadIdx.x;
+    const int grp = tid / RT;       // row slot within the workgroup
+    const int t = tid % RT;         // thread within the row
+    const int wave_in_row = t >> 6;
+    const long long row = (long long)blockIdx.x * RPB + grp;
+    const bool live = row < sp.rows;
+    const int nvec = sp.cols / E;
+
+    const char* xr = reinterpret_cast<const char*>(sp.x) + (live ? row : 0) * (long long)sp.cols * TI::kBytes;
+    char* yr = reinterpret_cast<char*>(sp.y) + (live ? row : 0) * (long long)sp.cols * TO::kBytes;
+
+    float v[VPT][E];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int j = i * RT + t;
+        if (live && j < nvec) {
+            VecIn<TI>::load(xr + (long long)j * E * TI::kBytes, v[i]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[i][e] = -INFINITY;
+        }
+    }
+
+    // pass 1 over the slice: its maximum, then its exponentials and their sum
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e) m = fmaxf(m, v[i][e]);
+    const float mref = (m == -INFINITY) ? 0.f : m;
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            v[i][e] = __builtin_amdgcn_exp2f((v[i][e] - mref) * kSmLog2e);
+            if (e & 1) l1 += v[i][e];
+            else l0 += v[i][e];
+        }
+    const float m_slice = m;
+    float l = l0 + l1;
+
+    // the row's state: lanes, then the waves of the row in a fixed order
+    sm_wave_merge(m, l);
+    if constexpr (WPR > 1) {
+        if ((tid & 63) == 0) {
+            s_m[grp][wave_in_row] = m;
+            s_l[grp][wave_in_row] = l;
+        }
+        __syncthreads();
+        m = s_m[grp][0];
+        l = s_l[grp][0];
+#pragma unroll
+        for (int w = 1; w < WPR; ++w) sm_merge(m, l, s_m[grp][w], s_l[grp][w]);
+    }
+
+    // pass 2: y = e^(x - m_slice) * e^(m_slice - m) / l
+    const bool dead = !(l > 0.f);
+    const float s = dead ? 0.f : sm_rescale(m_slice, m) / l;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int j = i * RT + t;
+        if (live && j < nvec) store_scaled<TO, E>(yr + (long long)j * E * TO::kBytes, v[i], s);
+    }
+    if (live && t == 0 && sp.lse) sp.lse[row] = dead ? -INFINITY : m + __builtin_amdgcn_logf(l) * kLn2;
+}
+
+// ---------------------------------------------------------------- streamed rows
+
+// One workgroup of NT threads per row, any length. VEC: the row is a whole
+// number of 16-byte vectors; otherwise elements are read one at a time.
+template <typename TI, typename TO, int NT, bool VEC>
+__global__ __launch_bounds__(NT) void softmax_stream_kernel(SoftmaxParams sp) {
+    constexpr int E = VEC ? VecIn<TI>::kN : 1;
+    constexpr int U = 4;  // vectors in flight per thread per step
+    __shared__ float s_m[NT / 64], s_l[NT / 64];
+
+    const int t = threadIdx.x;
+    const long long row = blockIdx.x;
+    const int cols = sp.cols;
+    const int nvec = cols / E;
+    const char* xr = reinterpret_cast<const char*>(sp.x) + row * (long long)cols * TI::kBytes;
+    char* yr = reinterpret_cast<char*>(sp.y) + row * (long long)cols * TO::kBytes;
+
+    auto load = [&](int j, float* v) {
+        if constexpr (VEC) VecIn<TI>::load(xr + (long long)j * E * TI::kBytes, v);
+        else v[0] = VecIn<TI>::load1(xr + (long long)j * TI::kBytes);
+    };
+
+    // pass 1: running (m, l) of this thread's vectors, one update per vector
+    float m = -INFINITY, l = 0.f;
+    for (int j0 = t; j0 < nvec; j0 += U * NT) {
+        float v[U][E];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * NT;
+            if (j < nvec) {
+                load(j, v[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) v[u][e] = -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vm = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < E; ++e) vm = fmaxf(vm, v[u][e]);
+            const float mn = fmaxf(m, vm);
+            const float ref = (mn == -INFINITY) ? 0.f : mn;
+            float add = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) add += __builtin_amdgcn_exp2f((v[u][e] - ref) * kSmLog2e);
+            l = l * sm_rescale(m, ref) + add;
+            m = mn;
+        }
+    }
+
+    sm_wave_merge(m, l);
+    if constexpr (NT > 64) {
+        if ((t & 63) == 0) {
+            s_m[t >> 6] = m;
+            s_l[t >> 6] = l;
+        }
+        __syncthreads();
+        m = s_m[0];
+        l = s_l[0];
+#pragma unroll
+        for (int w = 1; w < NT / 64; ++w) sm_merge(m, l, s_m[w], s_l[w]);
+    }
+    const bool dead = !(l > 0.f);
+    const float inv = dead ? 0.f : 1.f / l;
+    const float mref = dead ? 0.f : m;
+
+    // pass 2: y = e^(x - m) / l
+    for (int j0 = t; j0 < nvec; j0 += U * NT) {
+        float v[U][E];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * NT;
+            if (j < nvec) load(j, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * NT;
+            if (j < nvec) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) v[u][e] = __builtin_amdgcn_exp2f((v[u][e] - mref) * kSmLog2e);
+                if constexpr (VEC) store_scaled<TO, E>(yr + (long long)j * E * TO::kBytes, v[u], inv);
+                else store1<TO>(yr + (long long)j * TO::kBytes, v[u][0] * inv);
+            }
+        }
+    }
+    if (t == 0 && sp.lse) sp.lse[row] = dead ? -INFINITY : m + __builtin_amdgcn_logf(l) * kLn2;
+}
+
+}  // namespace fa

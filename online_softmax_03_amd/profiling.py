@@ -34,10 +34,20 @@ ROOT = os.path.dirname(PKG)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def source_hash() -> str:
-    """sha256 over the HIP sources and the public header (kernel identity)."""
+# The sources that make up each profiled kernel: its device code, its
+# instantiations and the host code that launches it.
+KERNEL_SOURCES = {
+    "attn_fwd_kernel": ["attn_common.h", "attn_fwd_kernel.h", "attn_fwd_f32_kernel.h", "attn_merge.h",
+                        "fa_table.h", "kern_d128_bf16.hip", "kern_d128_f16.hip", "kern_d64_bf16.hip",
+                        "kern_d64_f16.hip", "kern_f32.hip", "kern_merge.hip", "fa_api.hip"],
+    "softmax": ["attn_common.h", "softmax_kernel.h", "softmax_table.h", "kern_softmax.hip", "softmax_api.hip"],
+}
+
+
+def source_hash(kernel: str = "attn_fwd_kernel") -> str:
+    """sha256 over the sources of one kernel (its identity for profiles)."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [os.path.join(ROOT, "include", "fa.h")]
+    files = [os.path.join(PKG, "csrc", f) for f in KERNEL_SOURCES[kernel]]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -45,19 +55,23 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(PROFILES, f"attn_fwd_kernel_{workload}_traffic.json")
+def traffic_file(workload: str, kernel: str = "attn_fwd_kernel") -> str:
+    return os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
 
 
-def current_traffic(workload: str):
+def current_traffic(workload: str, kernel: str = "attn_fwd_kernel"):
     """The measured traffic summary for `workload` if it matches the current
     kernel sources, else None."""
-    path = traffic_file(workload)
+    path = traffic_file(workload, kernel)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    return t if t.get("source_hash") == source_hash() else None
+    return t if t.get("source_hash") == source_hash(_family(kernel)) else None
+
+
+def _family(kernel: str) -> str:
+    return "softmax" if kernel.startswith("softmax") else "attn_fwd_kernel"
 
 
 def _copy(mib: int, reps: int) -> None:
@@ -86,8 +100,8 @@ def _counter_rows(d: str, counter: str, name_filter: str):
 
 
 def _summarize(a) -> None:
-    fetch = _counter_rows(a.fetch, "FETCH_SIZE", "attn_fwd_kernel")
-    write = _counter_rows(a.write, "WRITE_SIZE", "attn_fwd_kernel")
+    fetch = _counter_rows(a.fetch, "FETCH_SIZE", a.kernel)
+    write = _counter_rows(a.write, "WRITE_SIZE", a.kernel)
     cfetch = _counter_rows(a.copy_fetch, "FETCH_SIZE", a.copy_filter)
     cwrite = _counter_rows(a.copy_write, "WRITE_SIZE", a.copy_filter)
     if not (fetch and write and cfetch and cwrite):
@@ -100,8 +114,8 @@ def _summarize(a) -> None:
     write_kib = sum(write) / len(write)
     out = {
         "workload": a.workload,
-        "kernel": "attn_fwd_kernel",
-        "source_hash": source_hash(),
+        "kernel": a.kernel,
+        "source_hash": source_hash(_family(a.kernel)),
         "dispatches": {"fetch": len(fetch), "write": len(write)},
         "fetch_kib_per_dispatch_raw": fetch_kib,
         "write_kib_per_dispatch_raw": write_kib,
@@ -112,7 +126,7 @@ def _summarize(a) -> None:
         "hbm_write_bytes_per_launch": write_kib * w_factor * 1024.0,
         "commands": a.commands,
     }
-    path = a.out or traffic_file(a.workload)
+    path = a.out or traffic_file(a.workload, a.kernel)
     with open(path, "w") as f:
         json.dump(out, f, indent=2)
     print(json.dumps(out, indent=2))
@@ -125,7 +139,7 @@ def _report(a) -> None:
             stats.extend(csv.DictReader(fh))
     with open(a.bench) as fh:
         bench = json.loads([l for l in fh if l.startswith("{")][-1])
-    lines = [f"# attn_fwd_kernel on {a.workload} (MI355X)", "",
+    lines = [f"# {a.kernel} on {a.workload} (MI355X)", "",
              "Produced by (from the repository root, on one MI355X):", "", "```"]
     lines += a.command
     lines += ["```", "", "## rocprofv3 kernel statistics", "",
@@ -136,7 +150,7 @@ def _report(a) -> None:
     rf = bench["roofline"]
     lines += ["", "## bench.py line of the same run", "", "```json", json.dumps(bench, indent=1), "```", "",
               f"bench.py's own per-launch HIP-event average: {rf['avg_launch_ms']:.4f} ms; "
-              f"achieved {rf['achieved']} TFLOP/s = {100 * rf['frac']:.1f}% of {rf['peak']} TFLOP/s."]
+              f"achieved {rf['achieved']} {rf['unit']} = {100 * rf['frac']:.1f}% of {rf['peak']} {rf['unit']}."]
     if a.traffic and os.path.exists(a.traffic):
         with open(a.traffic) as fh:
             t = json.load(fh)
@@ -159,6 +173,7 @@ def main():
     c.add_argument("--reps", type=int, default=5)
     s = sub.add_parser("summarize")
     s.add_argument("--workload", required=True)
+    s.add_argument("--kernel", default="attn_fwd_kernel")
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
     s.add_argument("--copy-fetch", required=True)
@@ -169,12 +184,14 @@ def main():
     s.add_argument("--out", default=None)
     r = sub.add_parser("report")
     r.add_argument("--workload", required=True)
+    r.add_argument("--kernel", default="attn_fwd_kernel")
     r.add_argument("--stats", required=True)
     r.add_argument("--bench", required=True)
     r.add_argument("--traffic", default=None)
     r.add_argument("--command", nargs="*", default=[])
     r.add_argument("--out", required=True)
-    sub.add_parser("hash")
+    hs = sub.add_parser("hash")
+    hs.add_argument("--kernel", default="attn_fwd_kernel")
     a = ap.parse_args()
     if a.cmd == "copy":
         _copy(a.mib, a.reps)
@@ -183,7 +200,7 @@ def main():
     elif a.cmd == "report":
         _report(a)
     else:
-        print(source_hash())
+        print(source_hash(_family(a.kernel)))
 
 
 if __name__ == "__main__":

@@ -118,3 +118,49 @@ def generate(w: Workload, seed: Optional[int] = None, lens: Optional[torch.Tenso
         mask = mask_from_lengths(lens, w.N)
     return dict(q=q, k=k, v=v, mask=mask, lens=lens, scale=w.scale, causal=w.causal,
                 in_dtype=w.in_dtype, out_dtype=w.out_dtype, workload=w)
+
+
+# ---------------------------------------------------------------- row softmax
+
+@dataclasses.dataclass(frozen=True)
+class SoftmaxWorkload:
+    """A [rows][cols] matrix whose rows are softmaxed independently."""
+    name: str
+    rows: int
+    cols: int
+    in_dtype: str
+    out_dtype: str
+    dist: tuple              # ("normal", sd) or ("uniform", lo, hi), drawn in float32
+    masked_frac: float = 0.0  # fraction of entries set to -inf (drawn after the values)
+    seed: int = 0
+
+    def algorithmic_bytes(self) -> int:
+        """x read once, y and the float32 LSE written once."""
+        eb = {"f32": 4, "bf16": 2, "f16": 2}
+        return self.rows * self.cols * (eb[self.in_dtype] + eb[self.out_dtype]) + 4 * self.rows
+
+    def with_shape(self, **kw) -> "SoftmaxWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+SOFTMAX_WORKLOADS = [
+    # rows of attention-score length (one per query of the headline attention
+    # shape's sequence length), logits with standard deviation 2
+    SoftmaxWorkload("sm_bf16_r32768_c8192", 32768, 8192, "bf16", "bf16", ("normal", 2.0), seed=2000),
+    # vocabulary-sized rows in float32: too long for registers, streamed
+    SoftmaxWorkload("sm_f32_r1024_c131072", 1024, 131072, "f32", "f32", ("normal", 4.0), seed=2001),
+]
+SOFTMAX_BY_NAME = {w.name: w for w in SOFTMAX_WORKLOADS}
+
+
+def generate_softmax(w: SoftmaxWorkload, seed: Optional[int] = None) -> torch.Tensor:
+    """x [rows][cols] (CPU, contiguous, in_dtype). Values are drawn in float32
+    from a generator seeded per workload, then a Bernoulli(masked_frac) draw
+    per entry replaces some by -inf, then the matrix is rounded to in_dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed if seed is None else seed)
+    x = _draw(gen, (w.rows, w.cols), w.dist)
+    if w.masked_frac > 0:
+        drop = torch.rand((w.rows, w.cols), generator=gen) < w.masked_frac
+        x = x.masked_fill(drop, float("-inf"))
+    return x.to(DTYPES[w.in_dtype]).contiguous()

@@ -131,3 +131,21 @@ def _split(**kw):
 ])
 def test_splitkv_invalid_arguments_rejected_on_host(kw, status):
     assert _split(**kw) == status
+
+
+def _sm(**kw):
+    a = dict(x=P, y=P, lse=P, rows=4, cols=64, in_dtype=BF16, out_dtype=BF16, stream=None)
+    a.update(kw)
+    return capi.fa_softmax_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), capi.FA_ERR_NULL), (dict(y=None), capi.FA_ERR_NULL),
+    (dict(rows=0), capi.FA_ERR_SHAPE), (dict(cols=0), capi.FA_ERR_SHAPE), (dict(rows=-3), capi.FA_ERR_SHAPE),
+    (dict(rows=1 << 31), capi.FA_ERR_SHAPE), (dict(rows=1 << 30, cols=1 << 11), capi.FA_ERR_SHAPE),
+    (dict(in_dtype=BF16, out_dtype=F16), capi.FA_ERR_DTYPE), (dict(in_dtype=F32, out_dtype=BF16), capi.FA_ERR_DTYPE),
+    (dict(in_dtype=5), capi.FA_ERR_DTYPE),
+    (dict(x=P + 2), capi.FA_ERR_ALIGN), (dict(y=P + 8), capi.FA_ERR_ALIGN), (dict(lse=P + 1), capi.FA_ERR_ALIGN),
+])
+def test_softmax_invalid_arguments_rejected_on_host(kw, status):
+    assert _sm(**kw) == status
