@@ -7,6 +7,8 @@ Python binding) never does, and the two share no code.
 - `attention(...)`: float64 three-pass safe-softmax attention (plain C).
 - `softmax_rows(x)`: float64 three-pass safe softmax of every row of a matrix
   (the standalone row-softmax operation).
+- `attention_bwd(...)`: float64 gradients dQ, dK, dV of the attention forward
+  (numpy, one head at a time).
 - `softmax_ref.safe_softmax`, `softmax_ref.online_softmax`,
   `softmax_ref.online_two_pass`, `softmax_ref.online_attention`,
   `softmax_ref.merge_states`: score-level and blocked references used to pin
@@ -14,4 +16,5 @@ Python binding) never does, and the two share no code.
 """
 from .attention import attention, build, load, max_threads  # noqa: F401
 from .softmax_rows import softmax_rows  # noqa: F401
+from .attention_bwd import attention_bwd  # noqa: F401
 from . import softmax_ref  # noqa: F401
