@@ -7,6 +7,11 @@ A step is one attention forward (one fa_fwd call) over the whole workload,
 inputs already resident in HBM. Prints ONE JSON line. The default workload is
 bf16, causal, d=128, N=8192, B=2, H=32.
 
+--bwd times the backward (one fa_bwd call per step: the D/LSE pass, the
+dK/dV kernel and the dQ kernel) on the forward's output, with nominal
+FLOPs 2.5x the forward's (the five products S, dP, dV, dK, dQ; the kernels
+also recompute S and dP once more, which is not counted).
+
 --workload sm_* times the standalone row softmax instead (one fa_softmax_fwd
 call per step; HBM-bound, reported in GB/s of algorithmic traffic: x read
 once, y and LSE written once).
@@ -45,6 +50,7 @@ def parse():
     ap.add_argument("--tile", default=None, help="block_r,block_c")
     ap.add_argument("--shape", default=None, help="B,H,N")
     ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--bwd", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -240,8 +246,20 @@ def main():
         ws = torch.empty(capi.fa_splitkv_workspace_bytes(w.B, w.H, w.N, w.d, splits), dtype=torch.uint8,
                          device=dev)
 
+    if args.bwd:
+        if splits is not None or args.tile:
+            sys.exit("--bwd takes neither --num-splits nor --tile")
+        fo, flse = A.attention_fwd(q, k, v, scale=w.scale, causal=w.causal, key_padding_mask=mask)
+        dout = W.generate_dout(w).to(dev)
+        grads = tuple(torch.empty(q.shape, dtype=q.dtype, device=dev) for _ in range(3))
+        bws = torch.empty(capi.fa_bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
     def step():
-        if splits is None:
+        if args.bwd:
+            A.attention_bwd(q, k, v, fo, dout, flse, scale=w.scale, causal=w.causal, key_padding_mask=mask,
+                            workspace=bws, out=grads)
+        elif splits is None:
             A.attention_fwd(q, k, v, scale=w.scale, causal=w.causal, key_padding_mask=mask,
                             out_dtype=out_dt, tile=tile, out=o, lse=lse)
         else:
@@ -252,13 +270,14 @@ def main():
     wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
 
-    flops = w.nominal_flops()
+    flops = w.nominal_flops() * (2.5 if args.bwd else 1.0)
     value = flops * args.steps / wall / 1e12
     achieved = flops / avg_launch_s / 1e12
     peak = PEAK_TFLOPS[w.in_dtype]
-    hbm_bytes, hbm_detail = traffic(w.name) if splits is None else (None, None)
+    hbm_bytes, hbm_detail = traffic(w.name) if (splits is None and not args.bwd) else (None, None)
     result = {
-        "metric": "attention fwd TFLOP/s and % of MFMA bf16 peak (causal, d=128, N=8192)",
+        "metric": ("attention bwd TFLOP/s (nominal 2.5x the forward's FLOPs) and % of MFMA bf16 peak"
+                   if args.bwd else "attention fwd TFLOP/s and % of MFMA bf16 peak (causal, d=128, N=8192)"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -272,14 +291,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "key_padding": w.key_padding, "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
-                   "block_r": tile[0], "block_c": tile[1], "num_splits": splits, "flops_per_step": flops},
+                   "block_r": tile[0], "block_c": tile[1], "num_splits": splits, "pass": "bwd" if args.bwd else "fwd",
+                   "flops_per_step": flops},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": hbm_bytes, "traffic_detail": hbm_detail,
-                     "kernel": KERNEL_PREFIX, "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                     "kernel": "attn_bwd (prep + dkdv + dq)" if args.bwd else KERNEL_PREFIX,
+                     "avg_launch_ms": round(avg_launch_s * 1e3, 4),
                      "min_launch_ms": round(min(launch_ms), 4)},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.bwd:
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -166,6 +166,50 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Attention backward from the saved LSE. The forward keeps no N x N matrix,
+ * so the scores are recomputed tile by tile and the probabilities recovered
+ * from the LSE the forward returned, P = exp(scale * Q K^T - LSE) over the
+ * allowed keys, with no second online pass ("Online Softmax 算法详解"
+ * section 8.3; the online-softmax interview card, section 四, point ③). With
+ * D_i = sum_t dO_it O_it the gradients are the chain rule through O = P V
+ * and the row softmax:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q.
+ * Masked keys receive dK = dV = 0; rows with no allowed key (LSE = -inf)
+ * contribute nothing and receive dQ = 0. Products run on bf16/fp16 MFMA with
+ * float32 accumulation; every gradient element is accumulated by one lane
+ * and stored once (no atomics, deterministic).
+ */
+
+/* fa_bwd_workspace_bytes — device workspace fa_bwd needs: per (b, h), two
+ * floats per query padded to a multiple of 64 queries,
+ * B * H * ceil(N / 64) * 512 bytes. 0 for invalid sizes. Host only. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * fa_bwd — gradients of fa_fwd.
+ *   q, k, v, o, dout  [B][H][N][d] in_dtype, device, 16-byte aligned; o is
+ *             the forward's output (in the input dtype) and dout the
+ *             gradient with respect to it
+ *   lse       [B][H][N] float32: the forward's LSE (natural log; -inf on
+ *             rows with no allowed key)
+ *   dq, dk, dv  [B][H][N][d] grad_dtype, device, 16-byte aligned (written)
+ *   B, H, N, d, scale, causal, key_padding_mask  as for fa_fwd (the same
+ *             values the forward was called with)
+ *   in_dtype  BF16 or F16;  grad_dtype  in_dtype or F32
+ *   workspace device memory of at least fa_bwd_workspace_bytes(B, H, N)
+ *             bytes, 16-byte aligned, owned by the caller, overwritten
+ *   stream    hipStream_t, or NULL
+ * Enqueues three kernels (per-row D and LSE, then dK/dV, then dQ). Calls
+ * that share a workspace must be ordered on the device. Returns FA_OK or a
+ * negative fa_status; nothing is launched on error.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+           float scale, int causal, const uint8_t* key_padding_mask, int in_dtype,
+           int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_softmax_fwd — softmax of every row of a matrix, with the online
  * normaliser.
  *

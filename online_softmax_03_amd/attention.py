@@ -92,3 +92,53 @@ def attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: floa
     if st != capi.FA_OK:
         raise FaError(st)
     return out, lse
+
+
+def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+                  lse: torch.Tensor, scale: float | None = None, causal: bool = False,
+                  key_padding_mask: torch.Tensor | None = None, grad_dtype: torch.dtype | None = None,
+                  workspace: torch.Tensor | None = None, out=None):
+    """dQ, dK, dV of `attention_fwd` from its output `o` and `lse` and the
+    output gradient `dout` (all [B, H, N, d] in q's dtype, bf16 or fp16; lse
+    [B, H, N] float32). grad_dtype defaults to q.dtype (float32 allowed).
+    `out` may give preallocated (dq, dk, dv). Returns (dq, dk, dv)."""
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must all be [B, H, N, d] with the same shape")
+    if any(not t.is_cuda or t.device != q.device for t in (q, k, v, o, dout, lse)):
+        raise ValueError("all tensors must be on the same GPU")
+    if q.dtype not in (torch.bfloat16, torch.float16) or any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must share a dtype among bfloat16, float16")
+    if any(not t.is_contiguous() for t in (q, k, v, o, dout, lse)):
+        raise ValueError("inputs must be contiguous")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a [B, H, N] float32 tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    grad_dtype = q.dtype if grad_dtype is None else grad_dtype
+    if grad_dtype not in (q.dtype, torch.float32):
+        raise ValueError("grad_dtype must be q.dtype or float32")
+    mask_ptr = None
+    if key_padding_mask is not None:
+        if key_padding_mask.shape != (B, N) or key_padding_mask.device != q.device:
+            raise ValueError("key_padding_mask must be [B, N] on the same device")
+        key_padding_mask = key_padding_mask.to(torch.uint8).contiguous()
+        mask_ptr = key_padding_mask.data_ptr()
+    need = capi.fa_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = (torch.empty(q.shape, dtype=grad_dtype, device=q.device) for _ in range(3))
+    else:
+        dq, dk, dv = out
+        if any(t.shape != q.shape or t.dtype != grad_dtype or not t.is_contiguous() or t.device != q.device
+               for t in out):
+            raise ValueError("out must be three contiguous [B, H, N, d] tensors of grad_dtype")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = capi.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                     mask_ptr, _DT[q.dtype], _DT[grad_dtype], workspace.data_ptr(),
+                     workspace.numel() * workspace.element_size(), stream)
+    if st != capi.FA_OK:
+        raise FaError(st)
+    return dq, dk, dv

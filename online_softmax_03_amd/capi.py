@@ -33,7 +33,8 @@ FA_MAX_SPLITS = 64
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_default_tile", "fa_tile_supported", "fa_splitkv_workspace_bytes",
-           "fa_splitkv_num_splits", "fa_fwd_splitkv", "fa_softmax_fwd", "fa_strerror")
+           "fa_splitkv_num_splits", "fa_fwd_splitkv", "fa_bwd_workspace_bytes", "fa_bwd", "fa_softmax_fwd",
+           "fa_strerror")
 
 
 class fa_tile(ctypes.Structure):
@@ -72,6 +73,11 @@ def library():
             lib.fa_splitkv_num_splits.argtypes = [_I, _I, _I, _I, _I]
             lib.fa_fwd_splitkv.restype = _I
             lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:-1] + [_I, _P, ctypes.c_size_t, _P]
+            lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+            lib.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I]
+            lib.fa_bwd.restype = _I
+            lib.fa_bwd.argtypes = ([_P] * 9 + [_I, _I, _I, _I, ctypes.c_float, _I, _P, _I, _I, _P,
+                                                ctypes.c_size_t, _P])
             lib.fa_softmax_fwd.restype = _I
             lib.fa_softmax_fwd.argtypes = [_P, _P, _P, ctypes.c_longlong, _I, _I, _I, _P]
             lib.fa_strerror.restype = ctypes.c_char_p
@@ -119,6 +125,16 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask,
                    num_splits, workspace, workspace_bytes, stream) -> int:
     return library().fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask,
                                     in_dtype, out_dtype, num_splits, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_workspace_bytes(B, H, N) -> int:
+    return int(library().fa_bwd_workspace_bytes(B, H, N))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_padding_mask, in_dtype, grad_dtype,
+           workspace, workspace_bytes, stream) -> int:
+    return library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_padding_mask,
+                            in_dtype, grad_dtype, workspace, workspace_bytes, stream)
 
 
 def fa_softmax_fwd(x, y, lse, rows, cols, in_dtype, out_dtype, stream) -> int:

@@ -41,6 +41,8 @@ KERNEL_SOURCES = {
                         "fa_table.h", "kern_d128_bf16.hip", "kern_d128_f16.hip", "kern_d64_bf16.hip",
                         "kern_d64_f16.hip", "kern_f32.hip", "kern_merge.hip", "fa_api.hip"],
     "softmax": ["attn_common.h", "softmax_kernel.h", "softmax_table.h", "kern_softmax.hip", "softmax_api.hip"],
+    "attn_bwd": ["attn_common.h", "attn_bwd_kernel.h", "bwd_table.h", "kern_bwd_bf16.hip", "kern_bwd_f16.hip",
+                 "bwd_api.hip"],
 }
 
 
@@ -71,7 +73,11 @@ def current_traffic(workload: str, kernel: str = "attn_fwd_kernel"):
 
 
 def _family(kernel: str) -> str:
-    return "softmax" if kernel.startswith("softmax") else "attn_fwd_kernel"
+    if kernel.startswith("softmax"):
+        return "softmax"
+    if kernel.startswith("attn_bwd"):
+        return "attn_bwd"
+    return "attn_fwd_kernel"
 
 
 def _copy(mib: int, reps: int) -> None:

@@ -120,6 +120,15 @@ def generate(w: Workload, seed: Optional[int] = None, lens: Optional[torch.Tenso
                 in_dtype=w.in_dtype, out_dtype=w.out_dtype, workload=w)
 
 
+def generate_dout(w: Workload, seed: Optional[int] = None) -> torch.Tensor:
+    """The output gradient dO for the backward of workload `w`: [B][H][N][d]
+    i.i.d. N(0, 1) in float32 from a generator seeded with w.seed + 7000 (or
+    `seed`), rounded to the input dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed + 7000 if seed is None else seed)
+    return _draw(gen, (w.B, w.H, w.N, w.d), ("normal", 1.0)).to(DTYPES[w.in_dtype]).contiguous()
+
+
 # ---------------------------------------------------------------- row softmax
 
 @dataclasses.dataclass(frozen=True)

@@ -149,3 +149,30 @@ def _sm(**kw):
 ])
 def test_softmax_invalid_arguments_rejected_on_host(kw, status):
     assert _sm(**kw) == status
+
+
+def test_bwd_workspace_bytes():
+    assert capi.fa_bwd_workspace_bytes(2, 3, 100) == 2 * 3 * 2 * 64 * 4 * 2  # ceil(100/64)=2 -> 4 groups
+    assert capi.fa_bwd_workspace_bytes(1, 1, 64) == 64 * 2 * 4
+    assert capi.fa_bwd_workspace_bytes(1, 1, 0) == 0
+    assert capi.fa_bwd_workspace_bytes(1 << 16, 1 << 16, 1 << 16) == 0
+
+
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, H=1, N=128, d=128, scale=0.125, causal=0,
+             key_padding_mask=None, in_dtype=BF16, grad_dtype=BF16, workspace=P, workspace_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return capi.fa_bwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), capi.FA_ERR_NULL), (dict(dout=None), capi.FA_ERR_NULL), (dict(lse=None), capi.FA_ERR_NULL),
+    (dict(dv=None), capi.FA_ERR_NULL), (dict(N=0), capi.FA_ERR_SHAPE), (dict(d=96), capi.FA_ERR_HEADDIM),
+    (dict(in_dtype=F32, grad_dtype=F32), capi.FA_ERR_DTYPE), (dict(grad_dtype=F16), capi.FA_ERR_DTYPE),
+    (dict(scale=-1.0), capi.FA_ERR_SCALE), (dict(o=P + 8), capi.FA_ERR_ALIGN), (dict(lse=P + 2), capi.FA_ERR_ALIGN),
+    (dict(workspace=None), capi.FA_ERR_WORKSPACE), (dict(workspace_bytes=128 * 2 * 4 - 4), capi.FA_ERR_WORKSPACE),
+    (dict(B=1 << 16, H=1 << 16, N=1 << 16), capi.FA_ERR_SHAPE),
+])
+def test_bwd_invalid_arguments_rejected_on_host(kw, status):
+    assert _bwd(**kw) == status
