@@ -18,7 +18,8 @@ from typing import Optional
 
 import torch
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+          "e4m3": torch.float8_e4m3fn}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -28,7 +29,7 @@ class Workload:
     H: int
     N: int
     d: int
-    in_dtype: str            # "f32" | "bf16" | "f16"
+    in_dtype: str            # "f32" | "bf16" | "f16" | "e4m3"
     out_dtype: str           # dtype of O; LSE is always float32
     causal: bool
     q_dist: tuple            # ("normal", sd) or ("uniform", lo, hi)
@@ -37,6 +38,8 @@ class Workload:
     key_padding: bool = False   # per-batch valid key length ~ U{0..N}
     block_c: Optional[int] = None  # forced key-tile width, None = library default
     seed: int = 0
+    # FP8 inputs only: per-tensor descales (real value = stored value * descale)
+    descale: tuple = (1.0, 1.0, 1.0)
 
     @property
     def scale(self) -> float:
@@ -70,6 +73,17 @@ WORKLOADS = [
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
+# FP8 (E4M3) forward: the headline shape with per-tensor scaling. Real inputs
+# ~ N(0, 1) are stored as value / descale with power-of-two descales (Q, K
+# 2^-6, V 2^-5), so the stored values spread over E4M3's normal range (|x| up
+# to ~300 < 448) and the dequantized logits match the bf16 headline's.
+FP8_WORKLOADS = [
+    Workload("fp8_causal_n8192_d128", 2, 32, 8192, 128, "e4m3", "bf16", True,
+             ("normal", 64.0), ("normal", 64.0), ("normal", 32.0), seed=3000,
+             descale=(2.0 ** -6, 2.0 ** -6, 2.0 ** -5)),
+]
+FP8_BY_NAME = {w.name: w for w in FP8_WORKLOADS}
+
 
 def _draw(gen: torch.Generator, shape, dist) -> torch.Tensor:
     if dist[0] == "normal":
@@ -102,7 +116,8 @@ def generate(w: Workload, seed: Optional[int] = None, lens: Optional[torch.Tenso
 
     Returns a dict with q, k, v (in_dtype), mask (uint8 [B][N] or None),
     lens (int64 [B] or None), scale (float32 value as a Python float), causal,
-    in_dtype / out_dtype names.
+    in_dtype / out_dtype names, descale (q, k, v). For "e4m3" the float32
+    draw is rounded to E4M3 by torch's conversion (nearest, ties to even).
     """
     gen = torch.Generator(device="cpu")
     gen.manual_seed(w.seed if seed is None else seed)
@@ -117,7 +132,7 @@ def generate(w: Workload, seed: Optional[int] = None, lens: Optional[torch.Tenso
             lens = key_lengths(gen, w.B, w.N)
         mask = mask_from_lengths(lens, w.N)
     return dict(q=q, k=k, v=v, mask=mask, lens=lens, scale=w.scale, causal=w.causal,
-                in_dtype=w.in_dtype, out_dtype=w.out_dtype, workload=w)
+                in_dtype=w.in_dtype, out_dtype=w.out_dtype, descale=w.descale, workload=w)
 
 
 def generate_dout(w: Workload, seed: Optional[int] = None) -> torch.Tensor:
