@@ -16,6 +16,9 @@ also recompute S and dP once more, which is not counted).
 call per step; HBM-bound, reported in GB/s of algorithmic traffic: x read
 once, y and LSE written once).
 
+--workload fp8_* times the FP8 (E4M3) forward (one fa_fwd_fp8 call per step,
+--max-offset 8 by default), against the dense FP8 MFMA peak.
+
 --shape replaces the workload's (B, H, N), or (rows, cols) for sm_* workloads (the workload is then reported as
 NAME@BxHxN). --num-splits S times the split-KV entry point instead (S = 0:
 the library's choice); a step is then its two launches, attention and merge,
@@ -34,7 +37,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # MI355X dense MFMA peak for bf16/fp16: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz.
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3,
+               # fp8: twice the 16-bit rate, 256 x 8192 FLOP/clk x 2.4 GHz
+               "e4m3": 5033.2}
 # MI355X HBM3E peak bandwidth.
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_causal_n8192_d128"
@@ -51,6 +56,7 @@ def parse():
     ap.add_argument("--shape", default=None, help="B,H,N")
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--bwd", action="store_true")
+    ap.add_argument("--max-offset", type=int, default=8, help="fp8 workloads: 8 or 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -59,16 +65,31 @@ def parse():
 
 def cpu_baseline(w, x, target_s):
     """Times the float64 oracle on a bounded random sample of rows of the same
-    workload, on this host's cores; reports nominal TFLOP/s of that sample."""
+    workload, on this host's cores; reports nominal TFLOP/s of that sample.
+    FP8 workloads run the FP8 oracle (E4M3 decode, then the same three-pass
+    attention)."""
     import numpy as np
     import oracle
 
     B, H, N, d = w.B, w.H, w.N, w.d
     rng = np.random.default_rng(123)
     threads = oracle.max_threads()
+    fp8 = w.in_dtype == "e4m3"
     # the oracle reads float32 containers of the input values; convert once
-    q, k, v = (x[n].float().numpy() for n in ("q", "k", "v"))
+    if fp8:
+        q, k, v = (x[n] for n in ("q", "k", "v"))
+    else:
+        q, k, v = (x[n].float().numpy() for n in ("q", "k", "v"))
     mask = None if x["mask"] is None else x["mask"].numpy()
+
+    def attention(b, h, rr):
+        sl = lambda t: t[b:b + 1, h:h + 1]  # noqa: E731
+        mk = None if mask is None else mask[b:b + 1]
+        if fp8:
+            oracle.fp8.attention_fp8(sl(q), sl(k), sl(v), x["scale"], *x["descale"], causal=x["causal"], mask=mk,
+                                     rows=rr, nthreads=threads)
+        else:
+            oracle.attention(sl(q), sl(k), sl(v), x["scale"], x["causal"], mk, rows=rr, nthreads=threads)
 
     def run(nrows):
         rows = np.sort(rng.choice(B * H * N, size=nrows, replace=False))
@@ -77,8 +98,7 @@ def cpu_baseline(w, x, target_s):
         for bh in np.unique(rows // N):
             b, h = divmod(int(bh), H)
             rr = rows[(rows // N) == bh] - bh * N
-            oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], x["scale"],
-                             x["causal"], None if mask is None else mask[b:b + 1], rows=rr, nthreads=threads)
+            attention(b, h, rr)
             keys = (rr + 1) if w.causal else np.full(rr.shape, N)
             flops += float(4.0 * d * keys.sum())
         return time.perf_counter() - t0, flops, nrows
@@ -89,7 +109,8 @@ def cpu_baseline(w, x, target_s):
     dt, fl, n = run(n2)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} rows of {w.name} drawn uniformly at random (seed 123), float64 three-pass "
-                      f"oracle, nominal 4*d*(allowed keys) FLOP per row, {dt:.1f} s"}
+                      f"oracle{' of the decoded E4M3 inputs' if fp8 else ''}, nominal 4*d*(allowed keys) FLOP "
+                      f"per row, {dt:.1f} s"}
 
 
 def traffic(workload, kernel=KERNEL_PREFIX):
@@ -219,7 +240,10 @@ def main():
     from online_softmax_03_amd import capi
     from online_softmax_03_amd import workloads as W
 
-    w = W.BY_NAME[args.workload]
+    fp8 = args.workload in W.FP8_BY_NAME
+    w = W.FP8_BY_NAME[args.workload] if fp8 else W.BY_NAME[args.workload]
+    if fp8 and (args.tile or args.num_splits is not None or args.bwd):
+        sys.exit("fp8 workloads take none of --tile, --num-splits, --bwd")
     if args.shape:
         B, H, N = (int(t) for t in args.shape.split(","))
         w = w.with_shape(B=B, H=H, N=N, name=f"{w.name}@{B}x{H}x{N}")
@@ -231,7 +255,9 @@ def main():
     o = torch.empty(q.shape, dtype=out_dt, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     tile = tuple(int(t) for t in args.tile.split(",")) if args.tile else None
-    if tile is None:
+    if fp8:
+        tile = (128, 64)  # the FP8 kernel's one shape: 4 waves x 32 queries, 64-key tiles
+    elif tile is None:
         st, tile = capi.fa_default_tile(w.N, w.d, A._DT[q.dtype], A._DT[out_dt], int(w.causal),
                                         int(mask is not None))
         assert st == 0
@@ -256,7 +282,11 @@ def main():
         torch.cuda.synchronize()
 
     def step():
-        if args.bwd:
+        if fp8:
+            A.attention_fwd_fp8(q, k, v, scale=w.scale, descale_q=w.descale[0], descale_k=w.descale[1],
+                                descale_v=w.descale[2], causal=w.causal, key_padding_mask=mask, out_dtype=out_dt,
+                                max_offset=args.max_offset, out=o, lse=lse)
+        elif args.bwd:
             A.attention_bwd(q, k, v, fo, dout, flse, scale=w.scale, causal=w.causal, key_padding_mask=mask,
                             workspace=bws, out=grads)
         elif splits is None:
@@ -274,10 +304,13 @@ def main():
     value = flops * args.steps / wall / 1e12
     achieved = flops / avg_launch_s / 1e12
     peak = PEAK_TFLOPS[w.in_dtype]
-    hbm_bytes, hbm_detail = traffic(w.name) if (splits is None and not args.bwd) else (None, None)
+    kernel = "attn_fwd_fp8_kernel" if fp8 else KERNEL_PREFIX
+    hbm_bytes, hbm_detail = traffic(w.name, kernel) if (splits is None and not args.bwd) else (None, None)
     result = {
         "metric": ("attention bwd TFLOP/s (nominal 2.5x the forward's FLOPs) and % of MFMA bf16 peak"
-                   if args.bwd else "attention fwd TFLOP/s and % of MFMA bf16 peak (causal, d=128, N=8192)"),
+                   if args.bwd else
+                   "FP8 attention fwd TFLOP/s and % of MFMA fp8 peak (causal, d=128, N=8192)" if fp8 else
+                   "attention fwd TFLOP/s and % of MFMA bf16 peak (causal, d=128, N=8192)"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -294,9 +327,10 @@ def main():
                    "block_r": tile[0], "block_c": tile[1], "num_splits": splits, "pass": "bwd" if args.bwd else "fwd",
                    "flops_per_step": flops},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        **({"max_offset": args.max_offset, "descale": list(w.descale)} if fp8 else {}),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": hbm_bytes, "traffic_detail": hbm_detail,
-                     "kernel": "attn_bwd (prep + dkdv + dq)" if args.bwd else KERNEL_PREFIX,
+                     "kernel": "attn_bwd (prep + dkdv + dq)" if args.bwd else kernel,
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4),
                      "min_launch_ms": round(min(launch_ms), 4)},
     }

@@ -62,7 +62,8 @@ typedef enum {
     FA_ERR_TILE = -7,      /* the requested tile configuration does not exist */
     FA_ERR_LAUNCH = -8,    /* the HIP runtime rejected the kernel launch */
     FA_ERR_SPLITS = -9,    /* num_splits outside [1, FA_MAX_SPLITS] */
-    FA_ERR_WORKSPACE = -10 /* workspace NULL, not 16-byte aligned, or too small */
+    FA_ERR_WORKSPACE = -10, /* workspace NULL, not 16-byte aligned, or too small */
+    FA_ERR_OFFSET = -11     /* fa_fwd_fp8: max_offset is neither 0 nor 8 */
 } fa_status;
 
 /* Largest number of key-range parts fa_fwd_splitkv accepts. */
@@ -164,6 +165,36 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int N, int d, float scale, int causal,
                    const uint8_t* key_padding_mask, int in_dtype, int out_dtype,
                    int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_fp8 — attention forward with FP8 (OCP E4M3) Q, K, V.
+ *
+ * The inputs are E4M3 bytes with per-tensor float32 descales: the real
+ * values are q * descale_q, k * descale_k, v * descale_v. The operation is
+ * fa_fwd's with S = scale * descale_q * descale_k * (q . k) and
+ * O = descale_v * sum_j softmax_j(S) v_j. Products run on gfx950's E4M3 MFMA
+ * with float32 accumulation, and P is rounded to E4M3 for the P V product.
+ * With max_offset = 8, the FP8 setting of "Online Softmax 算法详解" section 6,
+ * P is formed as 2^(S log2(e) - m log2(e) + 8) = 256 P, which places it in
+ * E4M3's normal range; the running sum is compensated (l = l' / 256) so the
+ * LSE is exact, and the output needs no extra factor. max_offset = 0 forms P
+ * in [0, 1] (the 16-bit setting) and is provided for comparison.
+ *   q, k, v   [B][H][N][d] E4M3 bytes, device, 16-byte aligned
+ *   o         [B][H][N][d] out_dtype (BF16, F16 or F32), 16-byte aligned
+ *   lse       [B][H][N] float32 (natural log; -inf on rows with no key)
+ *   d         128
+ *   scale, descale_q, descale_k, descale_v  > 0 and finite
+ *   causal, key_padding_mask, stream  as for fa_fwd
+ *   max_offset  8 or 0
+ * Returns FA_OK or a negative fa_status: FA_ERR_HEADDIM for d != 128,
+ * FA_ERR_DTYPE for another out_dtype, FA_ERR_SCALE when scale or a descale is
+ * not positive and finite, FA_ERR_OFFSET for another max_offset, and the
+ * other codes as fa_fwd.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, float descale_q, float descale_k,
+               float descale_v, int causal, const uint8_t* key_padding_mask, int out_dtype,
+               int max_offset, void* stream);
 
 /*
  * Attention backward from the saved LSE. The forward keeps no N x N matrix,

@@ -94,6 +94,53 @@ def attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: floa
     return out, lse
 
 
+def attention_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                      descale_q: float = 1.0, descale_k: float = 1.0, descale_v: float = 1.0,
+                      causal: bool = False, key_padding_mask: torch.Tensor | None = None,
+                      out_dtype: torch.dtype = torch.bfloat16, max_offset: int = 8,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Attention forward of FP8 E4M3 inputs (`fa_fwd_fp8`): q, k, v are
+    [B, H, N, 128] float8_e4m3fn (or uint8 holding E4M3 codes) whose real
+    values are value * descale. O = softmax(scale * (dq Q)(dk K)^T) (dv V) in
+    out_dtype (bfloat16, float16 or float32) and LSE [B, H, N] float32.
+    max_offset = 8 is the FP8 setting (P formed as 256 P before its E4M3
+    rounding); 0 rounds P in [0, 1]. Returns (o, lse)."""
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d] with the same shape")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if any(t.dtype not in (torch.float8_e4m3fn, torch.uint8) for t in (q, k, v)):
+        raise ValueError("q, k, v must be float8_e4m3fn (or uint8 E4M3 codes)")
+    if any(not t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out_dtype not in _DT:
+        raise ValueError("unsupported out_dtype")
+    mask_ptr = None
+    if key_padding_mask is not None:
+        if key_padding_mask.shape != (B, N) or key_padding_mask.device != q.device:
+            raise ValueError("key_padding_mask must be [B, N] on the same device")
+        key_padding_mask = key_padding_mask.to(torch.uint8).contiguous()
+        mask_ptr = key_padding_mask.data_ptr()
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, N, d] tensor of out_dtype")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous [B, H, N] float32 tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = capi.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                         float(scale), float(descale_q), float(descale_k), float(descale_v), int(bool(causal)),
+                         mask_ptr, _DT[out_dtype], int(max_offset), stream)
+    if st != capi.FA_OK:
+        raise FaError(st)
+    return out, lse
+
+
 def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
                   lse: torch.Tensor, scale: float | None = None, causal: bool = False,
                   key_padding_mask: torch.Tensor | None = None, grad_dtype: torch.dtype | None = None,

@@ -41,6 +41,7 @@ KERNEL_SOURCES = {
                         "fa_table.h", "kern_d128_bf16.hip", "kern_d128_f16.hip", "kern_d64_bf16.hip",
                         "kern_d64_f16.hip", "kern_f32.hip", "kern_merge.hip", "fa_api.hip"],
     "softmax": ["attn_common.h", "softmax_kernel.h", "softmax_table.h", "kern_softmax.hip", "softmax_api.hip"],
+    "attn_fwd_fp8": ["attn_common.h", "attn_fwd_fp8_kernel.h", "fp8_table.h", "kern_fp8.hip", "fp8_api.hip"],
     "attn_bwd": ["attn_common.h", "attn_bwd_kernel.h", "bwd_table.h", "kern_bwd_bf16.hip", "kern_bwd_f16.hip",
                  "bwd_api.hip"],
 }
@@ -77,6 +78,8 @@ def _family(kernel: str) -> str:
         return "softmax"
     if kernel.startswith("attn_bwd"):
         return "attn_bwd"
+    if kernel.startswith("attn_fwd_fp8"):
+        return "attn_fwd_fp8"
     return "attn_fwd_kernel"
 
 

@@ -23,7 +23,7 @@ P = 1 << 20  # a 16-byte-aligned stand-in address; never dereferenced in these t
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_names_every_status():
-    names = {s: capi.fa_strerror(s) for s in range(-10, 1)}
+    names = {s: capi.fa_strerror(s) for s in range(-11, 1)}
     assert names[0] == "ok"
     assert len(set(names.values())) == len(names)
     assert capi.fa_strerror(-99) == "unknown status"
@@ -176,3 +176,24 @@ def _bwd(**kw):
 ])
 def test_bwd_invalid_arguments_rejected_on_host(kw, status):
     assert _bwd(**kw) == status
+
+
+def _fp8(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=128, scale=0.125, descale_q=1.0, descale_k=1.0,
+             descale_v=1.0, causal=0, key_padding_mask=None, out_dtype=BF16, max_offset=8, stream=None)
+    a.update(kw)
+    return capi.fa_fwd_fp8(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), capi.FA_ERR_NULL), (dict(v=None), capi.FA_ERR_NULL), (dict(lse=None), capi.FA_ERR_NULL),
+    (dict(B=0), capi.FA_ERR_SHAPE), (dict(N=-1), capi.FA_ERR_SHAPE), (dict(d=64), capi.FA_ERR_HEADDIM),
+    (dict(out_dtype=9), capi.FA_ERR_DTYPE),
+    (dict(scale=0.0), capi.FA_ERR_SCALE), (dict(descale_q=-1.0), capi.FA_ERR_SCALE),
+    (dict(descale_k=float("inf")), capi.FA_ERR_SCALE), (dict(descale_v=float("nan")), capi.FA_ERR_SCALE),
+    (dict(max_offset=4), capi.FA_ERR_OFFSET), (dict(max_offset=-8), capi.FA_ERR_OFFSET),
+    (dict(k=P + 8), capi.FA_ERR_ALIGN), (dict(lse=P + 2), capi.FA_ERR_ALIGN),
+    (dict(B=1 << 16, H=1 << 16, N=1 << 16), capi.FA_ERR_SHAPE),
+])
+def test_fp8_invalid_arguments_rejected_on_host(kw, status):
+    assert _fp8(**kw) == status
