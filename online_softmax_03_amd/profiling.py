@@ -11,6 +11,13 @@
         run of bench.py: the attention kernel's launch statistics next to the
         bench line measured in the same process.
 
+    python -m online_softmax_03_amd.profiling tiles --run LABEL BENCH_JSON PMC_DIR ... \\
+        --command CMD ... --out FILE
+        writes the tile-choice table: for each run, the bench line's achieved
+        TFLOP/s next to rocprofv3 SQ/GRBM counters of the same configuration
+        (MFMA busy fraction, effective clock, VALU and LDS instructions per
+        MFMA, LDS bank conflicts, registers, scratch).
+
     python -m online_softmax_03_amd.profiling summarize --workload NAME \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR [--out FILE]
         reads the rocprofv3 counter CSVs, scales the attention kernel's
@@ -174,6 +181,66 @@ def _report(a) -> None:
     print("\n".join(lines))
 
 
+# MI355X: 8 XCDs (GRBM counters are summed over them), 256 CUs x 4 SIMDs.
+N_XCD = 8
+N_SIMD = 1024
+TILE_COUNTERS = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "GRBM_COUNT"]
+
+
+def _kernel_counters(d: str):
+    """{kernel name: {counter: mean over dispatches, plus registers and
+    scratch}} from a rocprofv3 counter-collection directory."""
+    per = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                k = per.setdefault(row["Kernel_Name"], {"_res": {}})
+                k.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                k["_res"] = {"VGPR_Count": row.get("VGPR_Count"), "Accum_VGPR_Count": row.get("Accum_VGPR_Count"),
+                             "SGPR_Count": row.get("SGPR_Count"), "Scratch_Size": row.get("Scratch_Size"),
+                             "LDS_Block_Size": row.get("LDS_Block_Size")}
+    out = {}
+    for name, k in per.items():
+        res = k.pop("_res")
+        out[name] = {c: sum(v) / len(v) for c, v in k.items()}
+        out[name].update(res)
+    return out
+
+
+def _tiles(a) -> None:
+    lines = ["# Tile choice: counters per configuration (MI355X)", "",
+             "Produced by (from the repository root, on one MI355X), per configuration:", "", "```"]
+    lines += a.command
+    lines += ["```", "",
+              "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); clock = "
+              "GRBM_GUI_ACTIVE / 8 / kernel time (the counters' own dispatch); TFLOP/s and % of peak from the bench "
+              "line of a separate, unprofiled run of the same configuration.", "",
+              "| configuration | kernel | TFLOP/s | % of peak | MFMA busy | clock (GHz) | VALU / MFMA | LDS / MFMA "
+              "| LDS bank conflicts | waves | VGPR (rocprofv3) | scratch |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for label, bench_path, pmc in a.run:
+        with open(bench_path) as fh:
+            bench = json.loads([l for l in fh if l.startswith("{")][-1])
+        rf = bench["roofline"]
+        kc = _kernel_counters(pmc)
+        name = max(kc, key=lambda n: kc[n].get("SQ_INSTS_MFMA", 0.0))
+        c = kc[name]
+        xcd_cycles = c["GRBM_GUI_ACTIVE"] / N_XCD
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * N_SIMD)
+        clock = xcd_cycles / (rf["avg_launch_ms"] * 1e-3) / 1e9
+        lines.append(
+            f"| {label} | `{name[:90]}` | {rf['achieved']:.1f} | {100 * rf['frac']:.1f}% | {100 * busy:.1f}% | "
+            f"{clock:.2f} | {c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:.2f} | "
+            f"{c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:.2f} | {c['SQ_LDS_BANK_CONFLICT']:.0f} | "
+            f"{c['SQ_WAVES']:.0f} | {c['VGPR_Count']} (+{c['Accum_VGPR_Count']} acc) | {c['Scratch_Size']} |")
+    lines += ["", "The clock column divides the counted cycles by the unprofiled launch time, so it is an estimate "
+              "of the clock the kernel ran at."]
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -199,6 +266,10 @@ def main():
     r.add_argument("--traffic", default=None)
     r.add_argument("--command", nargs="*", default=[])
     r.add_argument("--out", required=True)
+    t = sub.add_parser("tiles")
+    t.add_argument("--run", nargs=3, action="append", metavar=("LABEL", "BENCH_JSON", "PMC_DIR"), required=True)
+    t.add_argument("--command", nargs="*", default=[])
+    t.add_argument("--out", required=True)
     hs = sub.add_parser("hash")
     hs.add_argument("--kernel", default="attn_fwd_kernel")
     a = ap.parse_args()
@@ -208,6 +279,8 @@ def main():
         _summarize(a)
     elif a.cmd == "report":
         _report(a)
+    elif a.cmd == "tiles":
+        _tiles(a)
     else:
         print(source_hash(_family(a.kernel)))
 
