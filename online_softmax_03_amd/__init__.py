@@ -8,11 +8,21 @@ forward, `softmax.softmax_rows` that of the standalone row softmax;
 """
 from . import capi  # noqa: F401
 
-__all__ = ["capi", "attention_fwd", "softmax_rows"]
+__all__ = ["capi", "attention_fwd", "attention_fwd_fp8", "attention_bwd", "softmax_rows"]
 
 
 def attention_fwd(*args, **kwargs):
     from .attention import attention_fwd as f
+    return f(*args, **kwargs)
+
+
+def attention_fwd_fp8(*args, **kwargs):
+    from .attention import attention_fwd_fp8 as f
+    return f(*args, **kwargs)
+
+
+def attention_bwd(*args, **kwargs):
+    from .attention import attention_bwd as f
     return f(*args, **kwargs)
 
 
