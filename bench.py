@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--bwd", action="store_true")
     ap.add_argument("--max-offset", type=int, default=8, help="fp8 workloads: 8 or 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="after the timed steps, time 5 more launches each preceded by a write of this many MiB "
+                         "(0: skip); reported as roofline.flushed_*")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     return ap.parse_args()
@@ -152,6 +155,33 @@ def timed_steps(step, stream, steps, warmup):
     return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
+def flushed_launches(step, stream, n, flush_mib):
+    """`n` launches, each after a write of `flush_mib` MiB to a scratch buffer
+    (so the previous launch's inputs are no longer in the last-level cache),
+    timed with a HIP event pair on `stream` around the launch only. Returns
+    the per-launch ms list."""
+    import torch
+    scratch = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda:0")
+    times = []
+    for _ in range(n):
+        scratch.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del scratch
+    return times
+
+
+def _median(xs):
+    ys = sorted(xs)
+    m = len(ys) // 2
+    return ys[m] if len(ys) % 2 else 0.5 * (ys[m - 1] + ys[m])
+
+
 def softmax_cpu_baseline(w, x, target_s):
     """Times the float64 row-softmax oracle on a bounded random sample of rows
     of the same workload; reports GB/s of the workload's algorithmic bytes."""
@@ -199,9 +229,16 @@ def bench_softmax(args):
     wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup)
     avg_s = sum(launch_ms) / len(launch_ms) / 1e3
     nbytes = w.algorithmic_bytes()
-    kernel = "softmax_resident_kernel" if (w.cols % (4 if w.in_dtype == "f32" else 8) == 0 and
-                                           w.cols <= (32768 if w.in_dtype == "f32" else 65536)) \
-        else "softmax_stream_kernel"
+    # the library's choice: registers (up to 8192 16-byte vectors), registers
+    # + LDS (up to 20480 vectors for 16-bit inputs, 32768 for fp32), streamed
+    per_vec = 4 if w.in_dtype == "f32" else 8
+    nvec = w.cols // per_vec
+    if w.cols % per_vec != 0 or nvec > (32768 if w.in_dtype == "f32" else 20480):
+        kernel = "softmax_stream_kernel"
+    elif nvec > 8192:
+        kernel = "softmax_resident_lds_kernel"
+    else:
+        kernel = "softmax_resident_kernel"
     hbm_bytes, hbm_detail = traffic(w.name, kernel)
     result = {
         "metric": "row softmax HBM GB/s (algorithmic bytes: x read once, y and LSE written once)",
@@ -304,6 +341,7 @@ def main():
     # per-launch HIP events on the stream the kernel is launched on
     wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    flushed = flushed_launches(step, stream, 5, args.flush_mib) if args.flush_mib > 0 else None
 
     flops = w.nominal_flops() * (2.5 if args.bwd else 1.0)
     value = flops * args.steps / wall / 1e12
@@ -337,7 +375,10 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": hbm_bytes, "traffic_detail": hbm_detail,
                      "kernel": "attn_bwd (prep + dkdv + dq)" if args.bwd else kernel,
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4),
-                     "min_launch_ms": round(min(launch_ms), 4)},
+                     "median_launch_ms": round(_median(launch_ms), 4),
+                     "min_launch_ms": round(min(launch_ms), 4),
+                     **({"flushed_mib": args.flush_mib, "flushed_median_launch_ms": round(_median(flushed), 4),
+                         "flushed_min_launch_ms": round(min(flushed), 4)} if flushed else {})},
     }
     if not args.no_cpu_baseline and not args.bwd:
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

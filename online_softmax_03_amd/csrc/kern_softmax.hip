@@ -6,24 +6,36 @@
 namespace fa {
 
 #define FA_SM_RES(TI, IN, TO, OUT, WPR, RPB, VPT)                 \
-    SoftmaxEntry{IN, OUT, kSmResident, WPR, RPB, VPT, WPR * RPB * 64, \
+    SoftmaxEntry{IN, OUT, kSmResident, WPR, RPB, VPT, 0, WPR * RPB * 64, \
                  reinterpret_cast<const void*>(&softmax_resident_kernel<TI, TO, WPR, RPB, VPT>)}
+#define FA_SM_RES_LDS(TI, IN, TO, OUT, VPT, VLDS)                 \
+    SoftmaxEntry{IN, OUT, kSmResidentLds, 16, 1, VPT, VLDS, 1024, \
+                 reinterpret_cast<const void*>(&softmax_resident_lds_kernel<TI, TO, VPT, VLDS>)}
 #define FA_SM_STREAM(TI, IN, TO, OUT, VEC)                                               \
-    SoftmaxEntry{IN, OUT, (VEC) ? kSmStreamVec : kSmStreamScalar, 0, 0, 0, kSmStreamThreads, \
+    SoftmaxEntry{IN, OUT, (VEC) ? kSmStreamVec : kSmStreamScalar, 0, 0, 0, 0, kSmStreamThreads, \
                  reinterpret_cast<const void*>(&softmax_stream_kernel<TI, TO, kSmStreamThreads, (VEC) != 0>)}
 // Resident shapes, smallest first: (waves per row, rows per workgroup,
-// vectors per thread); capacity = waves * 64 * vectors 16-byte vectors.
-#define FA_SM_PAIR(TI, IN, TO, OUT)                                                           \
+// vectors per thread); capacity = waves * 64 * vectors 16-byte vectors. Then
+// the register + LDS shapes (1024 threads, VPT vectors per thread in
+// registers and 8 in LDS: 128 KB), whose register part is sized to 96 floats
+// per thread at most: capacity (VPT + 8) * 1024 vectors.
+#define FA_SM_RES_ALL(TI, IN, TO, OUT)                                                        \
     FA_SM_RES(TI, IN, TO, OUT, 1, 4, 1), FA_SM_RES(TI, IN, TO, OUT, 1, 4, 2),               \
         FA_SM_RES(TI, IN, TO, OUT, 1, 4, 4), FA_SM_RES(TI, IN, TO, OUT, 2, 2, 4),           \
         FA_SM_RES(TI, IN, TO, OUT, 4, 1, 4), FA_SM_RES(TI, IN, TO, OUT, 8, 1, 4),           \
-        FA_SM_RES(TI, IN, TO, OUT, 16, 1, 4), FA_SM_RES(TI, IN, TO, OUT, 16, 1, 8),         \
-        FA_SM_STREAM(TI, IN, TO, OUT, 1), FA_SM_STREAM(TI, IN, TO, OUT, 0)
+        FA_SM_RES(TI, IN, TO, OUT, 16, 1, 4), FA_SM_RES(TI, IN, TO, OUT, 16, 1, 8)
+#define FA_SM_STREAMS(TI, IN, TO, OUT) FA_SM_STREAM(TI, IN, TO, OUT, 1), FA_SM_STREAM(TI, IN, TO, OUT, 0)
+#define FA_SM_PAIR(TI, IN, TO, OUT)                                                                    \
+    FA_SM_RES_ALL(TI, IN, TO, OUT), FA_SM_RES_LDS(TI, IN, TO, OUT, 8, 8), FA_SM_RES_LDS(TI, IN, TO, OUT, 12, 8), \
+        FA_SM_STREAMS(TI, IN, TO, OUT)
+#define FA_SM_PAIR_F32(TI, IN, TO, OUT)                                                                  \
+    FA_SM_RES_ALL(TI, IN, TO, OUT), FA_SM_RES_LDS(TI, IN, TO, OUT, 16, 8), FA_SM_RES_LDS(TI, IN, TO, OUT, 24, 8), \
+        FA_SM_STREAMS(TI, IN, TO, OUT)
 
 static const SoftmaxEntry kSmEntries[] = {
     FA_SM_PAIR(BF16, FA_DTYPE_BF16, BF16, FA_DTYPE_BF16), FA_SM_PAIR(BF16, FA_DTYPE_BF16, F32, FA_DTYPE_F32),
     FA_SM_PAIR(F16, FA_DTYPE_F16, F16, FA_DTYPE_F16),     FA_SM_PAIR(F16, FA_DTYPE_F16, F32, FA_DTYPE_F32),
-    FA_SM_PAIR(F32, FA_DTYPE_F32, F32, FA_DTYPE_F32),
+    FA_SM_PAIR_F32(F32, FA_DTYPE_F32, F32, FA_DTYPE_F32),
 };
 const SoftmaxEntry* const kSoftmax = kSmEntries;
 const int kSoftmaxCount = (int)(sizeof(kSmEntries) / sizeof(kSmEntries[0]));

@@ -42,12 +42,14 @@ int fa_softmax_fwd(const void* x, void* y, float* lse, long long rows, int cols,
         if (e.in_dtype != in_dtype || e.out_dtype != out_dtype) continue;
         if (e.kind == fa::kSmResident) {
             if (vec && !pick && nvec <= (long long)e.wpr * 64 * e.vpt) pick = &e;
+        } else if (e.kind == fa::kSmResidentLds) {
+            if (vec && !pick && nvec <= (long long)(e.vpt + e.vlds) * e.threads) pick = &e;
         } else if (!pick && e.kind == (vec ? fa::kSmStreamVec : fa::kSmStreamScalar)) {
             pick = &e;
         }
     }
     if (!pick) return FA_ERR_DTYPE;
-    const long long rpb = pick->kind == fa::kSmResident ? pick->rpb : 1;
+    const long long rpb = pick->kind == fa::kSmResident ? pick->rpb : 1;  // one row per workgroup otherwise
     const long long grid = (rows + rpb - 1) / rpb;
     fa::SoftmaxParams sp;
     sp.x = x;

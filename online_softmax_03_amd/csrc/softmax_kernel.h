@@ -23,8 +23,12 @@
 //     commutative in IEEE arithmetic) and across the waves of the row (LDS,
 //     in a fixed order), and each thread rescales its exponentials by
 //     e^(m_slice - m) / l.
-//   softmax_stream_kernel: rows too long for registers, or whose length is
-//     not a whole number of 16-byte vectors. Pass 1 streams the row and keeps
+//   softmax_resident_lds_kernel: rows longer than the registers of one
+//     workgroup hold: each thread keeps part of its slice in registers and
+//     the rest in LDS (loaded there by LDS DMA, no registers in between), so
+//     x is still read from HBM once.
+//   softmax_stream_kernel: rows too long for registers and LDS, or whose
+//     length is not a whole number of 16-byte vectors. Pass 1 streams the row and keeps
 //     a running (m, l) per thread, updated per vector; pass 2 streams it again
 //     and writes y. One workgroup per row.
 #pragma once
@@ -56,6 +60,17 @@ struct VecIn<BF16> {
     __device__ static float load1(const char* p) {
         return __uint_as_float((u32)(*reinterpret_cast<const unsigned short*>(p)) << 16);
     }
+    __device__ static void cvt(const u32x4& u, float* v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(u[i] << 16);
+            v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+    __device__ static void load_lds(const FA_LDS char* p, float* v) {
+        const u32x4 u = *reinterpret_cast<const FA_LDS u32x4*>(p);
+        cvt(u, v);
+    }
 };
 
 template <>
@@ -67,6 +82,15 @@ struct VecIn<F16> {
         for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
     }
     __device__ static float load1(const char* p) { return (float)*reinterpret_cast<const _Float16*>(p); }
+    __device__ static void cvt(const u32x4& u, float* v) {
+        const f16x8 h = __builtin_bit_cast(f16x8, u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+    }
+    __device__ static void load_lds(const FA_LDS char* p, float* v) {
+        const u32x4 u = *reinterpret_cast<const FA_LDS u32x4*>(p);
+        cvt(u, v);
+    }
 };
 
 template <>
@@ -78,6 +102,14 @@ struct VecIn<F32> {
         for (int i = 0; i < 4; ++i) v[i] = f[i];
     }
     __device__ static float load1(const char* p) { return *reinterpret_cast<const float*>(p); }
+    __device__ static void cvt(const u32x4& u, float* v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(u[i]);
+    }
+    __device__ static void load_lds(const FA_LDS char* p, float* v) {
+        const u32x4 u = *reinterpret_cast<const FA_LDS u32x4*>(p);
+        cvt(u, v);
+    }
 };
 
 // N values times s, rounded to the output dtype and stored at p (N * size
@@ -96,6 +128,27 @@ __device__ __forceinline__ void store_scaled(char* p, const float* v, float s) {
             const u32x4 r = {pack2<T>(v[i] * s, v[i + 1] * s), pack2<T>(v[i + 2] * s, v[i + 3] * s),
                              pack2<T>(v[i + 4] * s, v[i + 5] * s), pack2<T>(v[i + 6] * s, v[i + 7] * s)};
             *reinterpret_cast<u32x4*>(p + 2 * i) = r;
+        }
+    }
+}
+
+// As store_scaled, through a buffer resource at per-lane byte offset
+// voffset (stores outside the resource are dropped by the hardware).
+template <typename T, int N>
+__device__ __forceinline__ void store_scaled_buf(__amdgpu_buffer_rsrc_t r, u32 voffset, const float* v, float s) {
+    if constexpr (T::kBytes == 4) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const u32x4 q = {__float_as_uint(v[i] * s), __float_as_uint(v[i + 1] * s),
+                             __float_as_uint(v[i + 2] * s), __float_as_uint(v[i + 3] * s)};
+            __builtin_amdgcn_raw_buffer_store_b128(q, r, voffset + 4 * i, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 8) {
+            const u32x4 q = {pack2<T>(v[i] * s, v[i + 1] * s), pack2<T>(v[i + 2] * s, v[i + 3] * s),
+                             pack2<T>(v[i + 4] * s, v[i + 5] * s), pack2<T>(v[i + 6] * s, v[i + 7] * s)};
+            __builtin_amdgcn_raw_buffer_store_b128(q, r, voffset + 2 * i, 0, 0);
         }
     }
 }
@@ -214,6 +267,138 @@ __global__ __launch_bounds__(WPR * RPB * 64) void softmax_resident_kernel(Softma
         if (live && j < nvec) store_scaled<TO, E>(yr + (long long)j * E * TO::kBytes, v[i], s);
     }
     if (live && t == 0 && sp.lse) sp.lse[row] = dead ? -INFINITY : m + __builtin_amdgcn_logf(l) * kLn2;
+}
+
+// ---------------------------------------------------------------- resident rows, registers + LDS
+
+// One workgroup of 1024 threads per row. Thread t holds vectors j = i*1024 + t
+// for i < VPT in registers and for VPT <= i < VPT + VLDS in LDS, at byte
+// ((i - VPT)*1024 + t)*16 of the workgroup's buffer: a wave's LDS DMA writes
+// 64 consecutive 16-byte slots, so each thread reads back only what its own
+// wave loaded (no barrier needed for that), and consecutive lanes read
+// consecutive 16-byte slots (no bank conflicts). The LDS part is read twice
+// (maximum and sum, then output) and its exponentials are recomputed on the
+// second read instead of being stored.
+template <typename TI, typename TO, int VPT, int VLDS>
+__global__ __launch_bounds__(1024) void softmax_resident_lds_kernel(SoftmaxParams sp) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int NT = 1024;
+    constexpr int E = VecIn<TI>::kN;
+    constexpr int NW = NT / 64;
+    __shared__ __attribute__((aligned(1024))) char s_x[VLDS * NT * 16];
+    __shared__ float s_m[NW], s_l[NW];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const long long row = blockIdx.x;
+    const int nvec = sp.cols / E;
+    const char* xr = reinterpret_cast<const char*>(sp.x) + row * (long long)sp.cols * TI::kBytes;
+    char* yr = reinterpret_cast<char*>(sp.y) + row * (long long)sp.cols * TO::kBytes;
+
+    // Buffer resources over the row, addressed by per-lane byte offsets only
+    // (the hardware's range check covers the per-lane offset, not a scalar
+    // one): vector j of x at j * 16. Vectors past the end of the row fall
+    // outside the resource (read as zero, stores dropped) and are excluded
+    // from the maximum and the sum by j < nvec.
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)xr, 0, nvec * 16, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc((void*)yr, 0, nvec * E * TO::kBytes, kBufferFlags);
+    const u32 xoff = (u32)t * 16u;
+    const u32 yoff = (u32)t * (E * TO::kBytes);
+    // LDS part first, so its loads are in flight while the register part loads.
+#pragma unroll
+    for (int k = 0; k < VLDS; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (FA_LDS void*)(s_x + (k * NT + wave * 64) * 16), 16,
+                                                 xoff + (u32)((VPT + k) * NT) * 16u, 0, 0, 0);
+    float v[VPT][E];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + (u32)(i * NT) * 16u, 0, 0);
+        VecIn<TI>::cvt(u, v[i]);
+        if (!(i * NT + t < nvec)) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[i][e] = -INFINITY;
+        }
+    }
+    wait_vmcnt0();
+    auto lds_vec = [&](int k, float* w) {
+        const int j = (VPT + k) * NT + t;
+        if (j < nvec) {
+            VecIn<TI>::load_lds((const FA_LDS char*)s_x + (k * NT + t) * 16, w);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) w[e] = -INFINITY;
+        }
+    };
+
+    // the slice's maximum over both parts, then its exponentials and their sum
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e) m = fmaxf(m, v[i][e]);
+    // (the LDS loops stay rolled: one vector in flight keeps the register
+    // part's budget)
+#pragma clang loop unroll(disable)
+    for (int k = 0; k < VLDS; ++k) {
+        float w[E];
+        lds_vec(k, w);
+#pragma unroll
+        for (int e = 0; e < E; ++e) m = fmaxf(m, w[e]);
+    }
+    const float mref = (m == -INFINITY) ? 0.f : m;
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            v[i][e] = __builtin_amdgcn_exp2f((v[i][e] - mref) * kSmLog2e);
+            if (e & 1) l1 += v[i][e];
+            else l0 += v[i][e];
+        }
+#pragma clang loop unroll(disable)
+    for (int k = 0; k < VLDS; ++k) {
+        float w[E];
+        lds_vec(k, w);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float x = __builtin_amdgcn_exp2f((w[e] - mref) * kSmLog2e);
+            if (e & 1) l1 += x;
+            else l0 += x;
+        }
+    }
+    const float m_slice = m;
+    float l = l0 + l1;
+
+    // the row's state: lanes, then the waves in a fixed order
+    sm_wave_merge(m, l);
+    if (lane == 0) {
+        s_m[wave] = m;
+        s_l[wave] = l;
+    }
+    __syncthreads();
+    m = s_m[0];
+    l = s_l[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) sm_merge(m, l, s_m[w], s_l[w]);
+
+    // output: y = e^(x - m_slice) * e^(m_slice - m) / l
+    const bool dead = !(l > 0.f);
+    const float sc = dead ? 0.f : sm_rescale(m_slice, m) / l;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) store_scaled_buf<TO, E>(ry, yoff + (u32)(i * NT) * (E * TO::kBytes), v[i], sc);
+#pragma clang loop unroll(disable)
+    for (int k = 0; k < VLDS; ++k) {
+        float w[E];
+        lds_vec(k, w);
+#pragma unroll
+        for (int e = 0; e < E; ++e) w[e] = __builtin_amdgcn_exp2f((w[e] - mref) * kSmLog2e);
+        store_scaled_buf<TO, E>(ry, yoff + (u32)((VPT + k) * NT) * (E * TO::kBytes), w, sc);
+    }
+    if (t == 0 && sp.lse) sp.lse[row] = dead ? -INFINITY : m + __builtin_amdgcn_logf(l) * kLn2;
+#endif
 }
 
 // ---------------------------------------------------------------- streamed rows

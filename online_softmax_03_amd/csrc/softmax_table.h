@@ -14,12 +14,13 @@ struct SoftmaxParams {
     int cols;
 };
 
-enum { kSmResident = 0, kSmStreamVec = 1, kSmStreamScalar = 2 };
+enum { kSmResident = 0, kSmStreamVec = 1, kSmStreamScalar = 2, kSmResidentLds = 3 };
 constexpr int kSmStreamThreads = 256;
 
 struct SoftmaxEntry {
     int in_dtype, out_dtype, kind;
     int wpr, rpb, vpt;  // resident shapes only
+    int vlds;           // vectors per thread held in LDS (kSmResidentLds)
     int threads;
     const void* fn;
 };

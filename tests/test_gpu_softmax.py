@@ -2,9 +2,9 @@
 (needs a GPU).
 
 Every row of the small cases is compared element by element; the lengths
-cover each register-resident shape on both sides of its capacity, both
-streamed forms (a length that is not a whole number of 16-byte vectors, and
-rows longer than the registers hold), masked entries, rows with a single live
+cover each register-resident and register + LDS shape on both sides of its
+capacity, both streamed forms (a length that is not a whole number of
+16-byte vectors, and rows longer than registers and LDS hold), masked entries, rows with a single live
 entry and rows with none. The two full-size workloads are compared on sampled
 rows. y and LSE are pre-filled with NaN so that an unwritten element fails.
 
@@ -67,8 +67,11 @@ def compare(y, lse, x, out_dtype, what):
     return float(err.max()) if err.size else 0.0, el
 
 
+# register-resident capacities (16-bit elements): 512 ... 65536; register +
+# LDS shapes: 131072 and 163840 (16-bit), 98304 and 131072 (fp32); each
+# also one vector over, which moves to the next shape or the streamed form
 COLS = [1, 3, 4, 8, 24, 64, 100, 512, 520, 1024, 1032, 2048, 2056, 4096, 4104, 8192, 8200, 16384, 16392,
-        32768, 32776, 65536, 65544, 70001, 131072]
+        32768, 32776, 65536, 65544, 70001, 98304, 98308, 100000, 131072, 131076, 131080, 163840, 163848]
 
 
 @pytest.mark.parametrize("cols", COLS)
@@ -103,7 +106,7 @@ def test_large_magnitudes_and_ragged_row_count(in_dtype):
 
 
 @pytest.mark.parametrize("pair", [("bf16", "bf16"), ("f32", "f32"), ("f16", "f16")])
-@pytest.mark.parametrize("cols", [512, 70001])
+@pytest.mark.parametrize("cols", [512, 70001, 131072])
 def test_in_place(pair, cols):
     w = BASE.with_shape(rows=5, cols=cols, in_dtype=pair[0], out_dtype=pair[1], seed=3200)
     x = W.generate_softmax(w)
