@@ -54,6 +54,10 @@ KERNEL_SOURCES = {
 }
 
 
+# Sources that no kernel's timing or traffic depends on (error texts).
+HOST_ONLY_SOURCES = ["status.hip"]
+
+
 def source_hash(kernel: str = "attn_fwd_kernel") -> str:
     """sha256 over the sources of one kernel (its identity for profiles)."""
     h = hashlib.sha256()
