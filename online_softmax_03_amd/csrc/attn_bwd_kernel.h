@@ -22,8 +22,8 @@
 //     row-major K tile by ds_read_b64_tr_b16 and dS^T fed back as the B
 //     operand (the forward's P V step with K in place of V).
 //   attn_bwd_dkdv_kernel  one workgroup per key tile, walking the query
-//     tiles: K and V of the wave's 32 keys stay in registers, Q, dO and the
-//     tile's (lse2, D) stream through LDS; S = Q K^T and dP = dO V^T with one
+//     tiles: V of the wave's 32 keys stays in registers and K in LDS (loaded
+//     once), Q, dO and the tile's (lse2, D) stream through LDS; S = Q K^T and dP = dO V^T with one
 //     key per lane, dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
 //     by the transpose loads.
 //
@@ -370,8 +370,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dK, dV
 
+// At least two waves per SIMD: with K in LDS the kernel fits 256 registers.
 template <int D, int BQ, int NW, typename TI, typename TO, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_bwd_dkdv_kernel(
+    BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BQ == 32 || BQ == 64, "query tile");
@@ -390,9 +392,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
     constexpr int LPW = (LOADS + NW - 1) / NW;
     constexpr int SB = NQB * 256;        // the tile's (lse2, D) groups
 
-    // Two buffers, each Q, dO, then the stats groups.
+    // Two buffers, each Q, dO, then the stats groups; and the workgroup's K
+    // rows, read as the B operand of S = Q K^T (in LDS rather than registers,
+    // which leaves room for two waves per SIMD).
     __shared__ __attribute__((aligned(1024))) char buf0[2 * TILEB + SB];
     __shared__ __attribute__((aligned(1024))) char buf1[2 * TILEB + SB];
+    __shared__ __attribute__((aligned(1024))) char kbuf[BK * ROWB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -433,7 +438,27 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
             *reinterpret_cast<FA_LDS u32x4*>((FA_LDS char*)buf0 + off) = z;
             *reinterpret_cast<FA_LDS u32x4*>((FA_LDS char*)buf1 + off) = z;
         }
+#pragma unroll
+        for (int off = tid * 16; off < BK * ROWB; off += NT * 16)
+            *reinterpret_cast<FA_LDS u32x4*>((FA_LDS char*)kbuf + off) = z;
         __syncthreads();
+    }
+
+    // The wave's 32 K rows into its own part of kbuf (row-major, chunks
+    // swizzled as in the tiles); keys past N read as zero. Only this wave
+    // reads them, so its own wait for the loads (the first tile's) suffices.
+    {
+        constexpr int KLOADS = 32 * ROWB / 1024;  // wave loads per wave
+        const int kbytes = max(N - kw0, 0) * ROWB;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kg + (size_t)min(kw0, N) * ROWB), 0, kbytes, kBufferFlags);
+#pragma unroll
+        for (int R = 0; R < KLOADS; ++R) {
+            const int krow = R * RPI + lane / CH;
+            const u32 off = (u32)(krow * ROWB + (((lane % CH) ^ swz<CH>(krow)) * 16));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(kbuf + wave * 32 * ROWB + R * 1024), 16,
+                                                     off, 0, 0, 0);
+        }
     }
 
     u32 lane_off[LPW];
@@ -469,18 +494,16 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
         }
     };
 
-    // K^T and V^T as B operands: lane l holds key l%32, d = 16*dc + 8*(l/32) .. +7.
-    u32x4 kop[NDC], vop[NDC];
+    // V^T as a B operand held in registers: lane l holds key l%32, d = 16*dc +
+    // 8*(l/32) .. +7. K^T, the same layout, is read from kbuf when needed.
+    u32x4 vop[NDC];
     {
         const int kr = min(key, N - 1);
-        const char* ksrc = kg + (size_t)kr * ROWB + hh * 16;
         const char* vsrc = vg + (size_t)kr * ROWB + hh * 16;
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
-            kop[dc] = *reinterpret_cast<const u32x4*>(ksrc + dc * 32);
-            vop[dc] = *reinterpret_cast<const u32x4*>(vsrc + dc * 32);
-        }
+        for (int dc = 0; dc < NDC; ++dc) vop[dc] = *reinterpret_cast<const u32x4*>(vsrc + dc * 32);
     }
+    const FA_LDS char* kw = (const FA_LDS char*)kbuf + wave * 32 * ROWB + col * ROWB;
 
     f32x16 acc_dk[NDB], acc_dv[NDB];
 #pragma unroll
@@ -522,23 +545,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int dc = 0; dc < NDC; ++dc) {
-                const int off = (qb * 32 + col) * ROWB + (((2 * dc + hh) ^ sw_col) * 16);
+                const int coff = ((2 * dc + hh) ^ sw_col) * 16;
+                const int off = (qb * 32 + col) * ROWB + coff;
                 const u32x4 a = *reinterpret_cast<const FA_LDS u32x4*>(qt + off);
-                s = mfma32x32x16<TI>(a, kop[dc], s);
+                const u32x4 kb = *reinterpret_cast<const FA_LDS u32x4*>(kw + coff);
+                s = mfma32x32x16<TI>(a, kb, s);
                 const u32x4 g = *reinterpret_cast<const FA_LDS u32x4*>(dt + off);
                 dp = mfma32x32x16<TI>(g, vop[dc], dp);
-            }
-            float l2[16], dd[16];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 lv = *reinterpret_cast<const FA_LDS f32x4*>(st + qb * 256 + (8 * g + 4 * hh) * 4);
-                const f32x4 dv4 =
-                    *reinterpret_cast<const FA_LDS f32x4*>(st + qb * 256 + 128 + (8 * g + 4 * hh) * 4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    l2[4 * g + i] = lv[i];
-                    dd[4 * g + i] = dv4[i];
-                }
             }
             // ---- masks: invalid key (this lane's column), causal q < key.
             // Queries past N carry lse2 = +inf and need no test.
@@ -551,22 +564,26 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
                     s[r] = ok ? s[r] : -INFINITY;
                 }
             }
-            // ---- P = 2^(S c - lse2), dS = P (dP - D), both packed as B operands
+            // ---- P = 2^(S c - lse2), dS = P (dP - D), both packed as B
+            // operands; registers 4g..4g+3 are queries 8g + 4*hh .. +3, whose
+            // (lse2, D) are read from the stats group one f32x4 each
             u32x4 pb[2], sb[2];
-            {
-                float pr[16], ds[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
-                    ds[r] = pr[r] * (dp[r] - dd[r]);
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 lv = *reinterpret_cast<const FA_LDS f32x4*>(st + qb * 256 + (8 * g + 4 * hh) * 4);
+                const f32x4 dv4 =
+                    *reinterpret_cast<const FA_LDS f32x4*>(st + qb * 256 + 128 + (8 * g + 4 * hh) * 4);
+                float pr[4], ds[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + i], c, -lv[i]));
+                    ds[i] = pr[i] * (dp[4 * g + i] - dv4[i]);
                 }
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        pb[t][j] = pack2<TI>(pr[8 * t + 2 * j], pr[8 * t + 2 * j + 1]);
-                        sb[t][j] = pack2<TI>(ds[8 * t + 2 * j], ds[8 * t + 2 * j + 1]);
-                    }
+                const int t = g >> 1, j = 2 * (g & 1);
+                pb[t][j] = pack2<TI>(pr[0], pr[1]);
+                pb[t][j + 1] = pack2<TI>(pr[2], pr[3]);
+                sb[t][j] = pack2<TI>(ds[0], ds[1]);
+                sb[t][j + 1] = pack2<TI>(ds[2], ds[3]);
             }
             // ---- dV^T += dO^T P and dK^T += Q^T dS (transpose reads of the dO and Q tiles)
 #pragma unroll
