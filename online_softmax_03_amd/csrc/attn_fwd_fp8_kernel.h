@@ -269,12 +269,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
             }
         l_run += rs0 + rs1;
 
-        // ---- P'^T as E4M3: byte 16*kb + r holds register r of block kb
+        // ---- P'^T as E4M3: byte 16*kb + r holds register r of block kb. The
+        // first conversion of a word writes its low half and keeps the high
+        // half, which the second overwrites; starting from the bits of an
+        // input that is dead afterwards lets it convert in place.
         i32x8 pb;
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
             const int kb = w >> 2, r0 = 4 * (w & 3);
-            int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][r0], s[kb][r0 + 1], 0, false);
+            int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][r0], s[kb][r0 + 1], __float_as_int(s[kb][r0]), false);
             x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][r0 + 2], s[kb][r0 + 3], x, true);
             pb[w] = x;
         }
