@@ -11,12 +11,13 @@
         run of bench.py: the attention kernel's launch statistics next to the
         bench line measured in the same process.
 
-    python -m online_softmax_03_amd.profiling tiles --run LABEL BENCH_JSON PMC_DIR ... \\
-        --command CMD ... --out FILE
+    python -m online_softmax_03_amd.profiling tiles \\
+        --run LABEL BENCH_JSON PMC_DIR FETCH_DIR WRITE_DIR ... \\
+        --copy-fetch DIR --copy-write DIR --command CMD ... --out FILE
         writes the tile-choice table: for each run, the bench line's achieved
         TFLOP/s next to rocprofv3 SQ/GRBM counters of the same configuration
         (MFMA busy fraction, effective clock, VALU and LDS instructions per
-        MFMA, LDS bank conflicts, registers, scratch).
+        MFMA, LDS bank conflicts, HBM bytes and GB/s, registers, scratch).
 
     python -m online_softmax_03_amd.profiling summarize --workload NAME \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR [--out FILE]
@@ -213,33 +214,46 @@ def _kernel_counters(d: str):
 
 
 def _tiles(a) -> None:
+    cfetch = _counter_rows(a.copy_fetch, "FETCH_SIZE", "")
+    cwrite = _counter_rows(a.copy_write, "WRITE_SIZE", "")
+    known = a.copy_mib * 1024.0
+    f_factor, w_factor = known / max(cfetch), known / max(cwrite)
     lines = ["# Tile choice: counters per configuration (MI355X)", "",
              "Produced by (from the repository root, on one MI355X), per configuration:", "", "```"]
     lines += a.command
     lines += ["```", "",
               "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); clock = "
-              "GRBM_GUI_ACTIVE / 8 / kernel time (the counters' own dispatch); TFLOP/s and % of peak from the bench "
-              "line of a separate, unprofiled run of the same configuration.", "",
+              "GRBM_GUI_ACTIVE / 8 / the unprofiled launch time; HBM = (FETCH_SIZE x "
+              f"{f_factor:.3f} + WRITE_SIZE x {w_factor:.3f}) per launch (factors from a plain 1 GiB copy) "
+              "/ the unprofiled launch time. TFLOP/s and % of peak from the bench line of a separate, unprofiled "
+              "run of the same configuration.", "",
               "| configuration | kernel | TFLOP/s | % of peak | MFMA busy | clock (GHz) | VALU / MFMA | LDS / MFMA "
-              "| LDS bank conflicts | waves | VGPR (rocprofv3) | scratch |",
-              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
-    for label, bench_path, pmc in a.run:
+              "| LDS bank conflicts | HBM read + write (MiB) | HBM GB/s | VGPR (rocprofv3) | scratch |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for label, bench_path, pmc, fetch_dir, write_dir in a.run:
         with open(bench_path) as fh:
             bench = json.loads([l for l in fh if l.startswith("{")][-1])
         rf = bench["roofline"]
         kc = _kernel_counters(pmc)
         name = max(kc, key=lambda n: kc[n].get("SQ_INSTS_MFMA", 0.0))
         c = kc[name]
+        t = rf["avg_launch_ms"] * 1e-3
         xcd_cycles = c["GRBM_GUI_ACTIVE"] / N_XCD
         busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * N_SIMD)
-        clock = xcd_cycles / (rf["avg_launch_ms"] * 1e-3) / 1e9
+        clock = xcd_cycles / t / 1e9
+        fk = _counter_rows(fetch_dir, "FETCH_SIZE", name)
+        wk = _counter_rows(write_dir, "WRITE_SIZE", name)
+        rd = sum(fk) / len(fk) * f_factor * 1024.0
+        wr = sum(wk) / len(wk) * w_factor * 1024.0
         lines.append(
             f"| {label} | `{name[:90]}` | {rf['achieved']:.1f} | {100 * rf['frac']:.1f}% | {100 * busy:.1f}% | "
             f"{clock:.2f} | {c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:.2f} | "
             f"{c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:.2f} | {c['SQ_LDS_BANK_CONFLICT']:.0f} | "
-            f"{c['SQ_WAVES']:.0f} | {c['VGPR_Count']} (+{c['Accum_VGPR_Count']} acc) | {c['Scratch_Size']} |")
+            f"{rd / 2**20:.0f} + {wr / 2**20:.0f} | {(rd + wr) / t / 1e9:.0f} | "
+            f"{c['VGPR_Count']} (+{c['Accum_VGPR_Count']} acc) | {c['Scratch_Size']} |")
     lines += ["", "The clock column divides the counted cycles by the unprofiled launch time, so it is an estimate "
-              "of the clock the kernel ran at."]
+              "of the clock the kernel ran at. rocprofv3's VGPR_Count column is reported as is; the compiler's "
+              "register counts follow."]
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -271,7 +285,11 @@ def main():
     r.add_argument("--command", nargs="*", default=[])
     r.add_argument("--out", required=True)
     t = sub.add_parser("tiles")
-    t.add_argument("--run", nargs=3, action="append", metavar=("LABEL", "BENCH_JSON", "PMC_DIR"), required=True)
+    t.add_argument("--run", nargs=5, action="append",
+                   metavar=("LABEL", "BENCH_JSON", "PMC_DIR", "FETCH_DIR", "WRITE_DIR"), required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-mib", type=int, default=1024)
     t.add_argument("--command", nargs="*", default=[])
     t.add_argument("--out", required=True)
     hs = sub.add_parser("hash")
