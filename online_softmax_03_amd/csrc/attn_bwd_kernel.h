@@ -53,6 +53,7 @@ struct BwdParams {
     int n_qtiles;          // dQ kernel: ceil(N / B_r)
     int n_ktiles;          // dK/dV kernel: ceil(N / B_k)
     int xcd_remap;
+    int head_group;        // heads whose tiles are dealt together (>= 1)
     float c;               // scale * log2(e)
     float scale;
 };
@@ -151,8 +152,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
 
     int id = blockIdx.x;
     if (p.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-    const int bh = id / p.n_qtiles;
-    const int qt = p.n_qtiles - 1 - (id - bh * p.n_qtiles);
+    int bh, qt;
+    work_item(id, p.n_qtiles, p.B * p.H, p.head_group, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;
     const int q0 = qt * BR;
@@ -406,11 +407,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int hh = lane >> 5;
 
     // workgroup -> (batch*head, key tile); causal: the first key tiles see
-    // the most queries, and they come first.
+    // the most queries, and they come first (work_item's order with the tile
+    // index reversed).
     int id = blockIdx.x;
     if (p.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-    const int bh = id / p.n_ktiles;
-    const int ktile = id - bh * p.n_ktiles;
+    int bh, ktile;
+    work_item(id, p.n_ktiles, p.B * p.H, p.head_group, &bh, &ktile);
+    ktile = p.n_ktiles - 1 - ktile;
     const int b = bh / p.H;
     const int N = p.N;
     const int k0 = ktile * BK;

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "work_item.h"
+
 namespace fa {
 
 typedef unsigned int u32;
@@ -36,6 +38,7 @@ struct Params {
     int B, H, N;
     int n_qtiles;         // ceil(N / B_r)
     int xcd_remap;        // 1: group consecutive tiles of a head on one XCD
+    int head_group;       // heads whose query tiles are dealt together (>= 1)
     float c;              // scale * log2(e)
     // split-KV only: the key tiles of every query tile are cut into n_splits
     // contiguous parts; part s writes its normalised partial output and its

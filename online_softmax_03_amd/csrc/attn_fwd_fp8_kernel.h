@@ -45,6 +45,7 @@ struct ParamsFp8 {
     int B, H, N;
     int n_qtiles;
     int xcd_remap;
+    int head_group;       // heads whose query tiles are dealt together (>= 1)
     float c;              // scale * descale_q * descale_k * log2(e)
     float descale_v;
 };
@@ -90,8 +91,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
 
     int id = blockIdx.x;
     if (p.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-    const int bh = id / p.n_qtiles;
-    const int qt = p.n_qtiles - 1 - (id - bh * p.n_qtiles);
+    int bh, qt;
+    work_item(id, p.n_qtiles, p.B * p.H, p.head_group, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;
     const int q0 = qt * BR;

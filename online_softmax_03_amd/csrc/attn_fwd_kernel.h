@@ -96,8 +96,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         split = id % p.n_splits;
         id /= p.n_splits;
     }
-    const int bh = id / p.n_qtiles;
-    const int qt = p.n_qtiles - 1 - (id - bh * p.n_qtiles);
+    int bh, qt;
+    work_item(id, p.n_qtiles, p.B * p.H, p.head_group, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;
     const int q0 = qt * BR;

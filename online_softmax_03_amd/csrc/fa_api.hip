@@ -89,7 +89,8 @@ int check_common(const void* q, const void* k, const void* v, void* o, float* ls
 }
 
 void fill_params(fa::Params& prm, const void* q, const void* k, const void* v, void* o, float* lse,
-                 const uint8_t* mask, int B, int H, int N, float scale, long long n_qtiles, long long grid) {
+                 const uint8_t* mask, int B, int H, int N, float scale, int causal, long long n_qtiles,
+                 long long grid) {
     prm.q = q;
     prm.k = k;
     prm.v = v;
@@ -101,6 +102,7 @@ void fill_params(fa::Params& prm, const void* q, const void* k, const void* v, v
     prm.N = N;
     prm.n_qtiles = (int)n_qtiles;
     prm.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    prm.head_group = fa::head_group_for(B * H, causal);
     prm.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
     prm.n_splits = 1;
     prm.ws_o = nullptr;
@@ -152,7 +154,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
     if (rows > (1LL << 40) || (long long)N * d * 4 > INT32_MAX || grid > INT32_MAX) return FA_ERR_SHAPE;
 
     fa::Params prm;
-    fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, n_qtiles, grid);
+    fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, causal, n_qtiles, grid);
     void* args[] = {&prm};
     const hipError_t err = hipLaunchKernel(e->fn, dim3((unsigned)grid), dim3(e->nwaves * 64), args, 0,
                                            reinterpret_cast<hipStream_t>(stream));
@@ -207,7 +209,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
     float* ws_o = static_cast<float*>(workspace);
     float* ws_lse = ws_o + (size_t)num_splits * (size_t)rows * (size_t)d;
     fa::Params prm;
-    fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, n_qtiles, grid);
+    fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, causal, n_qtiles, grid);
     prm.n_splits = num_splits;
     prm.ws_o = ws_o;
     prm.ws_lse = ws_lse;

@@ -6,10 +6,13 @@
         counters (bytes the copy must read and write per dispatch are known).
 
     python -m online_softmax_03_amd.profiling report --workload NAME \\
-        --stats DIR --bench FILE [--traffic FILE] --command CMD --out FILE
+        --stats DIR --bench FILE [--traffic FILE] --command CMD \\
+        [--pmc DIR --pmc-command CMD] --out FILE
         writes the markdown summary of a `rocprofv3 --kernel-trace --stats`
         run of bench.py: the attention kernel's launch statistics next to the
-        bench line measured in the same process.
+        bench line measured in the same process; with --pmc, also the SQ/GRBM
+        counters of a separate `rocprofv3 --pmc` run (MFMA busy fraction,
+        effective clock, VALU and LDS instructions per MFMA, bank conflicts).
 
     python -m online_softmax_03_amd.profiling tiles \\
         --run LABEL BENCH_JSON PMC_DIR FETCH_DIR WRITE_DIR ... \\
@@ -45,12 +48,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 # The sources that make up each profiled kernel: its device code, its
 # instantiations and the host code that launches it.
 KERNEL_SOURCES = {
-    "attn_fwd_kernel": ["attn_common.h", "attn_fwd_kernel.h", "attn_fwd_f32_kernel.h", "attn_merge.h",
+    "attn_fwd_kernel": ["attn_common.h", "work_item.h", "attn_fwd_kernel.h", "attn_fwd_f32_kernel.h", "attn_merge.h",
                         "fa_table.h", "kern_d128_bf16.hip", "kern_d128_f16.hip", "kern_d64_bf16.hip",
                         "kern_d64_f16.hip", "kern_f32.hip", "kern_merge.hip", "fa_api.hip"],
-    "softmax": ["attn_common.h", "softmax_kernel.h", "softmax_table.h", "kern_softmax.hip", "softmax_api.hip"],
-    "attn_fwd_fp8": ["attn_common.h", "attn_fwd_fp8_kernel.h", "fp8_table.h", "kern_fp8.hip", "fp8_api.hip"],
-    "attn_bwd": ["attn_common.h", "attn_bwd_kernel.h", "bwd_table.h", "kern_bwd_bf16.hip", "kern_bwd_f16.hip",
+    "softmax": ["attn_common.h", "work_item.h", "softmax_kernel.h", "softmax_table.h", "kern_softmax.hip", "softmax_api.hip"],
+    "attn_fwd_fp8": ["attn_common.h", "work_item.h", "attn_fwd_fp8_kernel.h", "fp8_table.h", "kern_fp8.hip", "fp8_api.hip"],
+    "attn_bwd": ["attn_common.h", "work_item.h", "attn_bwd_kernel.h", "bwd_table.h", "kern_bwd_bf16.hip", "kern_bwd_f16.hip",
                  "bwd_api.hip"],
 }
 
@@ -181,6 +184,24 @@ def _report(a) -> None:
                   f"(raw KiB x copy-kernel factor: fetch {t['copy_calibration']['fetch_factor']:.3f}, "
                   f"write {t['copy_calibration']['write_factor']:.3f})",
                   f"- source hash of the kernel sources: `{t['source_hash']}`"]
+    if a.pmc:
+        avg_ms = {r["Name"]: float(r["AverageNs"]) / 1e6 for r in stats}
+        kc = _kernel_counters(a.pmc)
+        lines += ["", "## Counters (rocprofv3 --pmc, one run)", "", "```"] + (a.pmc_command or []) + [
+            "```", "",
+            "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); clock = "
+            "GRBM_GUI_ACTIVE / 8 / the kernel-trace average above.", "",
+            "| kernel | MFMA busy | clock (GHz) | VALU / MFMA | LDS / MFMA | LDS bank conflicts |",
+            "|---|---|---|---|---|---|"]
+        for name in sorted(kc, key=lambda n: -kc[n].get("SQ_INSTS_MFMA", 0.0)):
+            c = kc[name]
+            if not c.get("SQ_INSTS_MFMA") or name not in avg_ms:
+                continue
+            xcd_cycles = c["GRBM_GUI_ACTIVE"] / N_XCD
+            lines.append(f"| `{name[:80]}` | {100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (xcd_cycles * N_SIMD):.1f}% | "
+                         f"{xcd_cycles / (avg_ms[name] * 1e-3) / 1e9:.2f} | "
+                         f"{c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:.2f} | "
+                         f"{c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:.2f} | {c['SQ_LDS_BANK_CONFLICT']:.0f} |")
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -283,6 +304,8 @@ def main():
     r.add_argument("--bench", required=True)
     r.add_argument("--traffic", default=None)
     r.add_argument("--command", nargs="*", default=[])
+    r.add_argument("--pmc", default=None)
+    r.add_argument("--pmc-command", nargs="*", default=[])
     r.add_argument("--out", required=True)
     t = sub.add_parser("tiles")
     t.add_argument("--run", nargs=5, action="append",

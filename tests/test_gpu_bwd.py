@@ -69,6 +69,10 @@ SMALL = [
     ("f16_d64_n1", C5, dict(B=1, H=1, N=1, key_padding=False), None),
     ("bf16_d128_n31", C3, dict(B=1, H=1, N=31), None),
     ("bf16_d128_n64_causal", C3, dict(B=2, H=1, N=64), None),
+    # causal launches over 32 and 16 heads deal their tiles over groups of 4
+    # and 2 heads
+    ("bf16_causal_d128_h32_n300", C3, dict(B=2, H=16, N=300), None),
+    ("f16_keypad_causal_d64_h16_n600", C5, dict(B=2, H=8, N=600, causal=True), [600, 417]),
 ]
 
 

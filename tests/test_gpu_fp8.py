@@ -124,6 +124,7 @@ SMALL = [
     ("noncausal_n130_f32out", dict(B=1, H=2, N=130, causal=False, out_dtype="f32"), None),
     ("keypad_n257", dict(B=6, H=1, N=257, causal=False), [0, 1, 63, 64, 65, 257]),
     ("keypad_causal_n200", dict(B=3, H=2, N=200), [0, 100, 200]),
+    ("causal_h32_n300", dict(B=2, H=16, N=300), None),  # tiles dealt over groups of 4 heads
     ("unit_descale_n300", dict(B=1, H=2, N=300, q_dist=("normal", 1.0), k_dist=("normal", 1.0),
                                v_dist=("normal", 1.0), descale=(1.0, 1.0, 1.0)), None),
 ]

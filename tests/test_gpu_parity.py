@@ -34,6 +34,10 @@ SMALL = [
     ("bf16_causal_d64_n2", C2, dict(B=1, H=1, N=2, causal=True), None),
     ("bf16_d128_n31", C3, dict(B=1, H=1, N=31), None),
     ("f16_d64_n33_keypad", C5, dict(B=2, H=1, N=33), [32, 33]),
+    # causal launches over 32 and 16 heads deal their query tiles over groups
+    # of 4 and 2 heads
+    ("bf16_causal_d128_h32_n300", C3, dict(B=2, H=16, N=300), None),
+    ("f16_keypad_causal_d64_h16_n600", C5, dict(B=2, H=8, N=600, causal=True), [600, 417]),
 ]
 
 
