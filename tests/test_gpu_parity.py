@@ -176,3 +176,52 @@ def test_every_tile_shape(d, br, bc, causal):
     w = C[C3].with_shape(B=2, H=2, N=301, d=d, causal=causal)
     x = W.generate(w, lens=torch.tensor([301, 97]))
     U.check_full(x, tile=(br, bc), what=f"tile {br}x{bc} d={d} causal={causal}")
+
+
+# Logit patterns whose row maxima grow by far more than 2^8 (in exp2 units)
+# after a row's first key tile, so the running state is rescaled: in every
+# tile ("ramp", by 2^16 or more per tile), once in the second or third tile
+# ("spike_early"), only in the last tile ("spike_last") and in half of the
+# workgroups ("mixed": batch 0 random, batch 1 ramp). The ramp reaches 2^150
+# over 300 keys, far past the float32 range of an unrescaled sum.
+GROWTH = ["ramp", "spike_early", "spike_last", "mixed"]
+
+
+def _growing_logits(x, pattern):
+    q, k = x["q"].clone(), x["k"].clone()
+    N = q.shape[2]
+    if pattern in ("ramp", "mixed"):
+        sel = slice(None) if pattern == "ramp" else slice(1, 2)
+        q[sel] = 0
+        q[sel, ..., 0] = 1
+        k[sel, ..., 0] = (4.0 * torch.arange(N, dtype=torch.float32)).to(k.dtype)
+    else:
+        key = N - 1 if pattern == "spike_last" else 70
+        q[..., 0] = 8
+        k[..., key, 0] = 60
+    y = dict(x)
+    y["q"], y["k"] = q.contiguous(), k.contiguous()
+    return y
+
+
+@pytest.mark.parametrize("pattern", GROWTH)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("base,over", [(C3, dict(B=2, H=2, N=300)),
+                                       (C2, dict(B=2, H=2, N=300)),
+                                       (C5, dict(B=2, H=2, N=300, key_padding=False))],
+                         ids=["bf16_d128", "bf16_d64_f32out", "f16_d64"])
+def test_growing_logits_rescale(base, over, causal, pattern):
+    w = C[base].with_shape(causal=causal, **over)
+    x = _growing_logits(W.generate(w), pattern)
+    what = f"{base} {pattern} causal={causal}"
+    U.log(f"case {what}: B,H,N,d={w.B},{w.H},{w.N},{w.d}")
+    U.check_full(x, what=what)
+
+
+@pytest.mark.parametrize("pattern", ["ramp", "spike_last"])
+@pytest.mark.parametrize("base", [C3, C2])
+def test_growing_logits_split_kv(base, pattern):
+    w = C[base].with_shape(B=1, H=2, N=300, causal=True)
+    x = _growing_logits(W.generate(w), pattern)
+    U.log(f"case {base} {pattern} split-KV 3 parts")
+    U.check_full(x, what=f"{base} {pattern} split 3", num_splits=3)
