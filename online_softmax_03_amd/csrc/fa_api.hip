@@ -66,6 +66,12 @@ const fa::MergeEntry* find_merge(int d, int out_dtype) {
     return nullptr;
 }
 
+// Workgroups of the split-KV kernel that one compute unit holds at once (its
+// register use): 3 for the 16-bit d = 128 tile (4 waves of at most 168
+// VGPRs), 2 for the 16-bit d = 64 tile (8 waves of at most 128) and for the
+// fp32 tile.
+int split_wgs_per_cu(int d, int in_dtype) { return (in_dtype != FA_DTYPE_F32 && d == 128) ? 3 : 2; }
+
 // Workspace of the split-KV path: fp32 partial outputs [S][B*H*N][d], then
 // their LSEs [S][B*H*N]. 0 if the sizes are out of range.
 size_t splitkv_bytes(int B, int H, int N, int d, int S) {
@@ -179,10 +185,14 @@ int fa_splitkv_num_splits(int B, int H, int N, int d, int in_dtype) {
     const fa_tile t = default_tile(d, in_dtype);
     const long long grid = (long long)B * H * (((long long)N + t.block_r - 1) / t.block_r);
     const long long key_tiles = ((long long)N + t.block_c - 1) / t.block_c;
-    // Enough workgroups for two per compute unit (256 CUs), keeping at least
-    // four key tiles per part.
+    // Enough parts to fill every workgroup slot of the 256 CUs at once,
+    // keeping at least four key tiles per part and at most 8 parts (beyond
+    // that the merge, which reads every part's row, costs more than the
+    // extra parallelism gains: 1 x 1 x 8192 runs 287 TFLOP/s at 8 parts and
+    // 270 at 12).
+    const long long slots = 256LL * split_wgs_per_cu(d, in_dtype);
     long long s = 1;
-    while (s < FA_MAX_SPLITS && grid * s < 512 && key_tiles / (2 * s) >= 4) s *= 2;
+    while (s < 8 && grid * s < slots && key_tiles / (s + 1) >= 4) ++s;
     return (int)s;
 }
 

@@ -99,12 +99,25 @@ def test_splitkv_workspace_bytes():
 
 
 def test_splitkv_num_splits_heuristic():
-    # a full grid needs no split; a small one splits until ~512 workgroups,
-    # keeping at least four key tiles per part
+    # a full grid needs no split; a small one splits until its parts fill the
+    # 768 (d = 128, 16-bit) or 512 (d = 64) resident workgroup slots, keeping
+    # at least four key tiles per part, and into at most 8 parts
     assert capi.fa_splitkv_num_splits(2, 32, 8192, 128, BF16) == 1
-    s = capi.fa_splitkv_num_splits(1, 2, 4096, 128, BF16)
-    assert s > 1 and s & (s - 1) == 0 and s <= capi.FA_MAX_SPLITS
-    assert 1 * 2 * (4096 // 128) * s >= 512 or (4096 // 32) // (2 * s) < 4
+    assert capi.fa_splitkv_num_splits(1, 16, 8192, 128, BF16) == 1   # 1024 workgroups
+    assert capi.fa_splitkv_num_splits(1, 8, 8192, 128, BF16) == 2    # 512 -> 1024
+    assert capi.fa_splitkv_num_splits(1, 4, 8192, 128, BF16) == 3    # 256 -> 768
+    assert capi.fa_splitkv_num_splits(1, 2, 8192, 128, BF16) == 6    # 128 -> 768
+    assert capi.fa_splitkv_num_splits(1, 8, 2048, 64, BF16) == 8     # 64 -> 512 (32 key tiles / 8)
+    assert capi.fa_splitkv_num_splits(1, 1, 8192, 128, BF16) == 8    # 64 -> 512: at most 8 parts
+    assert capi.fa_splitkv_num_splits(1, 1, 2048, 64, BF16) == 8     # capped: 32 key tiles, 4 per part
+    for B, H, N, d in [(1, 2, 4096, 128), (1, 1, 8192, 128), (3, 5, 1000, 64), (1, 1, 300, 128)]:
+        s = capi.fa_splitkv_num_splits(B, H, N, d, BF16)
+        br, bc, slots = (128, 32, 768) if d == 128 else (256, 64, 512)
+        grid, tiles = B * H * -(-N // br), -(-N // bc)
+        assert 1 <= s <= 8
+        assert s == 1 or tiles // s >= 4                       # every part keeps four key tiles
+        assert grid * s >= slots or s == 8 or tiles // (s + 1) < 4   # and no fewer parts would do
+        assert s == 1 or grid * (s - 1) < slots
     assert capi.fa_splitkv_num_splits(1, 1, 64, 128, BF16) == 1  # too few key tiles to split
     assert capi.fa_splitkv_num_splits(1, 1, 0, 128, BF16) == capi.FA_ERR_SHAPE
     assert capi.fa_splitkv_num_splits(1, 1, 64, 80, BF16) == capi.FA_ERR_HEADDIM
