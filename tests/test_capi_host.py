@@ -65,6 +65,9 @@ def _fwd(**kw):
     (dict(tile=(96, 64)), capi.FA_ERR_TILE), (dict(tile=(128, 48)), capi.FA_ERR_TILE),
     (dict(tile=(-32, 64)), capi.FA_ERR_TILE),
     (dict(B=1 << 16, H=1 << 16, N=1 << 16), capi.FA_ERR_SHAPE),
+    # a row index times the bytes of a float32 row must fit in 31 bits: N = 2^22
+    # is one past the largest sequence at d = 128, N = 2^23 at d = 64
+    (dict(N=1 << 22), capi.FA_ERR_SHAPE), (dict(N=1 << 23, d=64), capi.FA_ERR_SHAPE),
 ])
 def test_invalid_arguments_rejected_on_host(kw, status):
     assert _fwd(**kw) == status

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+from online_softmax_03_amd import attention as A
 from online_softmax_03_amd import workloads as W
 from tests import gpu_util as U
 
@@ -126,6 +127,55 @@ def test_full_size_sampled_rows(name):
         # row 0 of every head attends to key 0 only: O = v_0, LSE = scale*q_0.k_0
         v0 = x["v"][:, :, 0].double().numpy()
         assert np.abs(O[:, :, 0] - v0).max() <= U.O_TOL[w.in_dtype]
+
+
+def test_largest_sequence_at_d128():
+    """N = 4194303, the largest N with N*d*4 < 2^31 at d = 128: Q and O rows
+    up to 1 GB from the head's start, K and V read from their last 8192 rows,
+    the only keys the mask allows (so the launch does 1.8e13 FLOP). Q is one
+    drawn 8192-row block repeated along N; K and V are zero outside the
+    allowed keys. The oracle sees the same rows against the 8192 allowed keys
+    (non-causal: the set of keys a row attends is all that matters)."""
+    dev = torch.device("cuda:0")
+    L, d = 8192, 128
+    N = (2**31 - 1) // (d * 4)
+    w = C[C3].with_shape(B=1, H=1, N=L, causal=False)
+    x = W.generate(w)
+    U.log(f"case largest N: B,H,N,d=1,1,{N},{d}, keys [{N - L}, {N}) allowed")
+    q = x["q"].to(dev).repeat(1, 1, -(-N // L), 1)[:, :, :N].contiguous()
+    k = torch.zeros((1, 1, N, d), dtype=q.dtype, device=dev)
+    v = torch.zeros_like(k)
+    k[:, :, N - L:] = x["k"].to(dev)
+    v[:, :, N - L:] = x["v"].to(dev)
+    mask = torch.zeros((1, N), dtype=torch.uint8, device=dev)
+    mask[:, N - L:] = 1
+    o = torch.full(q.shape, float("nan"), dtype=q.dtype, device=dev)
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev)
+    A.attention_fwd(q, k, v, scale=w.scale, causal=False, key_padding_mask=mask, out=o, lse=lse)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, L - 1, L, N // 2, N - L - 1, N - L, N - 2, N - 1],
+                                     g.integers(0, N, 40)]))
+    qs = torch.zeros((1, 1, L, d), dtype=x["q"].dtype)
+    qs[0, 0, :len(rows)] = x["q"][0, 0][torch.from_numpy(rows % L)]
+    Oref, Lref, fm = U.oracle.attention(qs, x["k"], x["v"], x["scale"], False, None, rows=np.arange(len(rows)))
+    ridx = torch.from_numpy(rows).to(dev)
+    Og = o[0, 0].index_select(0, ridx).float().cpu().numpy().astype(np.float64)
+    Lg = lse[0, 0].index_select(0, ridx).cpu().numpy().astype(np.float64)
+    e = U.compare(Og, Lg, Oref, Lref, fm, "bf16", "largest N")
+    U.log(f"  {len(rows)} rows up to {N - 1}: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+
+
+def test_long_causal_sequence_sampled_rows():
+    """Causal d = 128 at N = 262144 (one head, 2048 query tiles, K/V offsets
+    up to 64 MB), sampled rows against the oracle."""
+    w = C[C3].with_shape(B=1, H=1, N=262144)
+    x = W.generate(w)
+    U.log(f"case causal N={w.N}")
+    rows = U.sample_rows(w.B, w.H, w.N, 48, seed=13, causal=True)
+    O, L, _ = U.check_sampled(x, rows, what="causal N=262144")
+    assert not np.isnan(O).any() and not np.isnan(L).any()
 
 
 def test_nondefault_stream_and_repeat():
