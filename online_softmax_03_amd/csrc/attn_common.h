@@ -39,6 +39,7 @@ struct Params {
     int n_qtiles;         // ceil(N / B_r)
     int xcd_remap;        // 1: group consecutive tiles of a head on one XCD
     int head_group;       // heads whose query tiles are dealt together (>= 1)
+    int fair;             // 1: equal-progress wave priorities (see fa_api.hip)
     float c;              // scale * log2(e)
     // split-KV only: the key tiles of every query tile are cut into n_splits
     // contiguous parts; part s writes its normalised partial output and its

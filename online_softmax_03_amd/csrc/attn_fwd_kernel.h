@@ -333,6 +333,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     // Main loop, unrolled by two so each half names its buffer statically.
     if (n_tiles > 0) issue_tile(0, buf0);
     for (int it = 0; it < n_tiles; it += 2) {
+        if (p.fair) {
+            // Equal progress: a wave's issue priority falls with the share of
+            // its tiles done, so the waves furthest behind issue first.
+            const int quarter = (it * 4) / n_tiles;
+            if (quarter == 0) __builtin_amdgcn_s_setprio(3);
+            else if (quarter == 1) __builtin_amdgcn_s_setprio(2);
+            else if (quarter == 2) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
         wait_vmcnt0();     // this wave's loads of tile `it` have landed
         __syncthreads();   // ... everyone's, and tile it-1 (buffer 1) is no longer read
         if (it + 1 < n_tiles) issue_tile(it + 1, buf1);

@@ -66,11 +66,11 @@ const fa::MergeEntry* find_merge(int d, int out_dtype) {
     return nullptr;
 }
 
-// Workgroups of the split-KV kernel that one compute unit holds at once (its
-// register use): 3 for the 16-bit d = 128 tile (4 waves of at most 168
-// VGPRs), 2 for the 16-bit d = 64 tile (8 waves of at most 128) and for the
-// fp32 tile.
-int split_wgs_per_cu(int d, int in_dtype) { return (in_dtype != FA_DTYPE_F32 && d == 128) ? 3 : 2; }
+// Workgroups of the default-tile kernel (plain or split-KV) that one compute
+// unit holds at once (its register use): 3 for the 16-bit d = 128 tile (4
+// waves of at most 168 VGPRs), 2 for the 16-bit d = 64 tile (8 waves of at
+// most 128) and for the fp32 tile.
+int resident_wgs_per_cu(int d, int in_dtype) { return (in_dtype != FA_DTYPE_F32 && d == 128) ? 3 : 2; }
 
 // Workspace of the split-KV path: fp32 partial outputs [S][B*H*N][d], then
 // their LSEs [S][B*H*N]. 0 if the sizes are out of range.
@@ -109,6 +109,7 @@ void fill_params(fa::Params& prm, const void* q, const void* k, const void* v, v
     prm.n_qtiles = (int)n_qtiles;
     prm.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     prm.head_group = fa::head_group_for(B * H, causal);
+    prm.fair = 0;
     prm.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
     prm.n_splits = 1;
     prm.ws_o = nullptr;
@@ -161,6 +162,20 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 
     fa::Params prm;
     fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, causal, n_qtiles, grid);
+    // When every workgroup is resident from the start (the grid fits the 256
+    // CUs at once) and all have the same work (no causal or key mask), the
+    // launch ends when the slowest workgroup does. The SIMDs issue from the
+    // oldest wave first, so one of the co-resident workgroups of each CU
+    // finishes early and the other runs its last part alone (on the d = 64
+    // non-causal workload: half the workgroups end at 54-59 us, half at
+    // 76-81 us). Priorities that follow each wave's progress even this out
+    // (+2% there); with a causal mask the oldest workgroups hold the longest
+    // tiles and should finish first, so it stays off.
+    const fa_tile dt = default_tile(d, in_dtype);
+    prm.fair = (!causal && !key_padding_mask && t.block_r == dt.block_r && t.block_c == dt.block_c &&
+                grid <= 256LL * resident_wgs_per_cu(d, in_dtype))
+                   ? 1
+                   : 0;
     void* args[] = {&prm};
     const hipError_t err = hipLaunchKernel(e->fn, dim3((unsigned)grid), dim3(e->nwaves * 64), args, 0,
                                            reinterpret_cast<hipStream_t>(stream));
@@ -190,7 +205,7 @@ int fa_splitkv_num_splits(int B, int H, int N, int d, int in_dtype) {
     // that the merge, which reads every part's row, costs more than the
     // extra parallelism gains: 1 x 1 x 8192 runs 287 TFLOP/s at 8 parts and
     // 270 at 12).
-    const long long slots = 256LL * split_wgs_per_cu(d, in_dtype);
+    const long long slots = 256LL * resident_wgs_per_cu(d, in_dtype);
     long long s = 1;
     while (s < 8 && grid * s < slots && key_tiles / (s + 1) >= 4) ++s;
     return (int)s;
