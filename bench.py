@@ -346,6 +346,16 @@ def main():
     flops = w.nominal_flops() * (2.5 if args.bwd else 1.0)
     value = flops * args.steps / wall / 1e12
     achieved = flops / avg_launch_s / 1e12
+    effective = None
+    if x["lens"] is not None:
+        # allowed (query, key) pairs under the key mask (and the causal mask):
+        # the FLOPs the kernel must do, not the nominal count
+        n = torch.arange(w.N, dtype=torch.float64)
+        pairs = sum(float(torch.minimum(n + 1, torch.tensor(float(l))).sum()) if w.causal else float(w.N * l)
+                    for l in x["lens"].tolist()) * w.H
+        eff_flops = 4.0 * w.d * pairs * (2.5 if args.bwd else 1.0)
+        effective = {"flops_per_step": eff_flops, "tflops": round(eff_flops / avg_launch_s / 1e12, 2),
+                     "fraction_of_nominal": round(eff_flops / flops, 4)}
     peak = PEAK_TFLOPS[w.in_dtype]
     kernel = "attn_fwd_fp8_kernel" if fp8 else KERNEL_PREFIX
     hbm_bytes, hbm_detail = traffic(w.name, kernel) if (splits is None and not args.bwd) else (None, None)
@@ -370,6 +380,7 @@ def main():
                    "block_r": tile[0], "block_c": tile[1], "num_splits": splits, "pass": "bwd" if args.bwd else "fwd",
                    "flops_per_step": flops},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        **({"effective": effective} if effective else {}),
         **({"max_offset": args.max_offset, "descale": list(w.descale)} if fp8 else {}),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": hbm_bytes, "traffic_detail": hbm_detail,

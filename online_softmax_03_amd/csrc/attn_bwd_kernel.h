@@ -52,7 +52,7 @@ struct BwdParams {
     int n_g;               // 32-query groups per head, padded to an even count
     int n_qtiles;          // dQ kernel: ceil(N / B_r)
     int n_ktiles;          // dK/dV kernel: ceil(N / B_k)
-    int xcd_remap;
+    int xcd_remap;         // XcdMode: how workgroup ids spread over the 8 XCDs
     int head_group;        // heads whose tiles are dealt together (>= 1)
     float c;               // scale * log2(e)
     float scale;
@@ -150,10 +150,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
     const int col = lane & 31;
     const int hh = lane >> 5;
 
-    int id = blockIdx.x;
-    if (p.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-    int bh, qt;
-    work_item(id, p.n_qtiles, p.B * p.H, p.head_group, &bh, &qt);
+    int split, bh, qt;
+    schedule(blockIdx.x, gridDim.x, p.n_qtiles, p.B * p.H, 1, p.head_group, p.xcd_remap, &split, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;
     const int q0 = qt * BR;
@@ -409,10 +407,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // workgroup -> (batch*head, key tile); causal: the first key tiles see
     // the most queries, and they come first (work_item's order with the tile
     // index reversed).
-    int id = blockIdx.x;
-    if (p.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-    int bh, ktile;
-    work_item(id, p.n_ktiles, p.B * p.H, p.head_group, &bh, &ktile);
+    int split, bh, ktile;
+    schedule(blockIdx.x, gridDim.x, p.n_ktiles, p.B * p.H, 1, p.head_group, p.xcd_remap, &split, &bh, &ktile);
     ktile = p.n_ktiles - 1 - ktile;
     const int b = bh / p.H;
     const int N = p.N;

@@ -37,7 +37,7 @@ struct Params {
     const uint8_t* mask;  // [B][N] or nullptr
     int B, H, N;
     int n_qtiles;         // ceil(N / B_r)
-    int xcd_remap;        // 1: group consecutive tiles of a head on one XCD
+    int xcd_remap;        // XcdMode: how workgroup ids spread over the 8 XCDs
     int head_group;       // heads whose query tiles are dealt together (>= 1)
     int fair;             // 1: equal-progress wave priorities (see fa_api.hip)
     float c;              // scale * log2(e)

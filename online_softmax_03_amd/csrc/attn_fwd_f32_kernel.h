@@ -41,15 +41,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(Params p) {
     const int col = lane & 31;
     const int hh = lane >> 5;
 
-    int id = blockIdx.x;
-    if (p.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-    int split = 0;
-    if constexpr (SPLIT) {
-        split = id % p.n_splits;
-        id /= p.n_splits;
-    }
-    const int bh = id / p.n_qtiles;
-    const int qt = p.n_qtiles - 1 - (id - bh * p.n_qtiles);
+    int split, bh, qt;
+    schedule(blockIdx.x, gridDim.x, p.n_qtiles, p.B * p.H, SPLIT ? p.n_splits : 1, p.head_group, p.xcd_remap,
+             &split, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;
     const int q0 = qt * BR;

@@ -44,7 +44,7 @@ struct ParamsFp8 {
     const uint8_t* mask;  // [B][N] or nullptr
     int B, H, N;
     int n_qtiles;
-    int xcd_remap;
+    int xcd_remap;         // XcdMode: how workgroup ids spread over the 8 XCDs
     int head_group;       // heads whose query tiles are dealt together (>= 1)
     float c;              // scale * descale_q * descale_k * log2(e)
     float descale_v;
@@ -89,10 +89,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
     const int col = lane & 31;
     const int hh = lane >> 5;
 
-    int id = blockIdx.x;
-    if (p.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-    int bh, qt;
-    work_item(id, p.n_qtiles, p.B * p.H, p.head_group, &bh, &qt);
+    int split, bh, qt;
+    schedule(blockIdx.x, gridDim.x, p.n_qtiles, p.B * p.H, 1, p.head_group, p.xcd_remap, &split, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;
     const int q0 = qt * BR;

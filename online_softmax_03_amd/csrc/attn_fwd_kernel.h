@@ -89,15 +89,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     // from the last (largest causal extent) to the first, and with the remap
     // consecutive ids of one XCD (ids are dealt round-robin over 8 XCDs) cover
     // consecutive tiles, so the workgroups sharing a head's K/V share an L2.
-    int id = blockIdx.x;
-    if (p.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
-    int split = 0;
-    if constexpr (SPLIT) {
-        split = id % p.n_splits;
-        id /= p.n_splits;
-    }
-    int bh, qt;
-    work_item(id, p.n_qtiles, p.B * p.H, p.head_group, &bh, &qt);
+    int split, bh, qt;
+    schedule(blockIdx.x, gridDim.x, p.n_qtiles, p.B * p.H, SPLIT ? p.n_splits : 1, p.head_group, p.xcd_remap,
+             &split, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;
     const int q0 = qt * BR;

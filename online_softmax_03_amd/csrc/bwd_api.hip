@@ -93,7 +93,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     prm.n_g = (int)n_g;
     prm.n_qtiles = (int)n_qtiles;
     prm.n_ktiles = (int)n_ktiles;
-    prm.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    prm.xcd_remap = fa::xcd_mode_for(B * H, grid);
     prm.head_group = fa::head_group_for(B * H, causal);
     prm.c = (float)((double)scale * 1.4426950408889634074);
     prm.scale = scale;

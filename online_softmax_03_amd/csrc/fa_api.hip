@@ -107,7 +107,7 @@ void fill_params(fa::Params& prm, const void* q, const void* k, const void* v, v
     prm.H = H;
     prm.N = N;
     prm.n_qtiles = (int)n_qtiles;
-    prm.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    prm.xcd_remap = fa::xcd_mode_for(B * H, grid);
     prm.head_group = fa::head_group_for(B * H, causal);
     prm.fair = 0;
     prm.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)

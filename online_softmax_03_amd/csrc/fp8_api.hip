@@ -51,7 +51,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     prm.H = H;
     prm.N = N;
     prm.n_qtiles = (int)n_qtiles;
-    prm.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    prm.xcd_remap = fa::xcd_mode_for(B * H, grid);
     prm.head_group = fa::head_group_for(B * H, causal);
     prm.c = (float)((double)scale * descale_q * descale_k * 1.4426950408889634074);
     prm.descale_v = descale_v;

@@ -28,11 +28,52 @@ constexpr void work_item(int id, int n_tiles, int n_heads, int G, int* bh, int* 
     *tile = n_tiles - 1 - t;
 }
 
+// How workgroup ids are spread over the 8 XCDs. The hardware deals
+// workgroup ids round-robin: id b runs on XCD b % 8, and each XCD starts its
+// ids in increasing order.
+//   kXcdHeads (B*H a multiple of 8): XCD x takes heads x, x + 8, x + 16, ...
+//     whole (every tile of a head on one XCD, so its K and V are read into
+//     one L2), and heads of every batch alike, so work that differs by batch
+//     (key-padding lengths) is spread evenly over the XCDs.
+//   kXcdChunks (grid a multiple of 8 only): XCD x takes the x-th eighth of
+//     the items in head-major order (parts of at most two heads).
+//   kXcdNone: the ids as they come.
+enum XcdMode { kXcdNone = 0, kXcdChunks = 1, kXcdHeads = 2 };
+
+// Workgroup `block` of a grid of n_heads * n_tiles * n_splits -> (key-range
+// part `split`, batch*head `bh`, tile `tile`), by the XCD mode above and, on
+// each XCD, by work_item over that XCD's heads (group size G). Every block
+// in [0, grid) maps to a distinct triple; the split part varies fastest, so
+// the parts of one tile run side by side.
+constexpr void schedule(int block, int grid, int n_tiles, int n_heads, int n_splits, int G, int xcd_mode,
+                        int* split, int* bh, int* tile) {
+    if (xcd_mode == kXcdHeads) {
+        const int x = block & 7;
+        int k = block >> 3;
+        *split = k % n_splits;
+        k /= n_splits;
+        int j = 0;
+        work_item(k, n_tiles, n_heads / 8, G, &j, tile);
+        *bh = j * 8 + x;
+        return;
+    }
+    int id = block;
+    if (xcd_mode == kXcdChunks) id = (block & 7) * (grid >> 3) + (block >> 3);
+    *split = id % n_splits;
+    id /= n_splits;
+    work_item(id, n_tiles, n_heads, G, bh, tile);
+}
+
+// Host side: the XCD mode of a launch over n_heads heads and `grid`
+// workgroups.
+constexpr int xcd_mode_for(int n_heads, long long grid) {
+    return n_heads % 8 == 0 ? kXcdHeads : (grid % 8 == 0 ? kXcdChunks : kXcdNone);
+}
+
 // Host side: G for a launch over n_heads heads. Without a causal mask every
 // item has the same length and the order does not matter (G = 1). With one,
-// G = 2 when every XCD's share of the grid holds an even number of heads
-// (the shares hold n_heads / 8 heads each), so that no pair straddles two
-// XCDs. Measured on the causal d = 128, N = 8192, 64-head launch: +2%
+// G = 2 when every XCD holds an even number of heads (n_heads / 8 each under
+// kXcdHeads). Measured on the causal d = 128, N = 8192, 64-head launch: +2%
 // throughput for 1.5x the HBM reads (K/V re-read from outside the L2 when
 // two heads are streamed at once); G = 4 gained another 0-1% for 2-4x the
 // reads.

@@ -1,12 +1,14 @@
 """The work-item order of the attention kernels (CPU; the header is plain
 constexpr C++ and is compiled here with g++).
 
-Every launch maps workgroup ids onto (batch*head, tile) pairs through
-`work_item`; the checks below run that same function over many shapes and
-group sizes: every id must land on a distinct pair in range (a bijection),
-tiles must be dealt from the last to the first within every group, and the
-group size chosen for a launch must keep groups inside one XCD's share of the
-grid.
+Every launch maps workgroup ids onto (key-range part, batch*head, tile)
+through `schedule`, which spreads the heads over the 8 XCDs and orders each
+XCD's items with `work_item`; the checks below run those same functions over
+many shapes, part counts, group sizes and XCD modes: every id must land on a
+distinct triple in range (a bijection), tiles must be dealt from the last to
+the first within every group, the head mode must keep every head on the one
+XCD its index names, and the host's choices (group size, XCD mode) must fit
+the shape.
 """
 import os
 import shutil
@@ -69,6 +71,52 @@ int main() {
     fa::work_item(1, 4, 4, 2, &b1, &t1);
     fa::work_item(2, 4, 4, 2, &b2, &t2);
     if (!(b0 == 0 && t0 == 3 && b1 == 1 && t1 == 3 && b2 == 0 && t2 == 2)) { ++bad; printf("G=2 order\n"); }
+    // schedule: every XCD mode the host can pick, with key-range parts
+    const int splits[] = {1, 2, 3, 8};
+    for (int H : heads)
+        for (int nt : tiles)
+            for (int S : splits)
+                for (int G : {1, 2, 4})
+                    for (int mode = 0; mode < 3; ++mode) {
+                        const long long grid = (long long)H * nt * S;
+                        if (grid > 200000) continue;
+                        if (mode == fa::kXcdHeads && H % 8 != 0) continue;
+                        if (mode == fa::kXcdChunks && grid % 8 != 0) continue;
+                        std::vector<int> seen((size_t)grid, 0);
+                        std::vector<int> xcd_of_head((size_t)H, -1);
+                        bool ok = true;
+                        for (int b = 0; b < grid && ok; ++b) {
+                            int sp = -1, bh = -1, t = -1;
+                            fa::schedule(b, (int)grid, nt, H, S, G, mode, &sp, &bh, &t);
+                            if (sp < 0 || sp >= S || bh < 0 || bh >= H || t < 0 || t >= nt) {
+                                printf("schedule range H=%d nt=%d S=%d G=%d mode=%d b=%d\n", H, nt, S, G, mode, b);
+                                ok = false;
+                                break;
+                            }
+                            ++seen[((size_t)bh * nt + t) * S + sp];
+                            if (mode == fa::kXcdHeads) {
+                                // XCD b % 8 runs whole heads, those with bh % 8 == b % 8
+                                if (bh % 8 != b % 8) { printf("head %d on XCD %d\n", bh, b % 8); ok = false; }
+                            }
+                            if (mode != fa::kXcdNone) {
+                                int& x = xcd_of_head[(size_t)bh];
+                                if (mode == fa::kXcdHeads && x >= 0 && x != b % 8) { printf("head split over XCDs\n"); ok = false; }
+                                x = b % 8;
+                            }
+                        }
+                        for (int c : seen)
+                            if (ok && c != 1) { printf("schedule not a bijection H=%d nt=%d S=%d G=%d mode=%d\n", H, nt, S, G, mode); ok = false; }
+                        if (!ok) ++bad;
+                        ++cases;
+                    }
+    // the host's choice: heads mode exactly when the heads divide over the XCDs
+    for (int H = 1; H <= 64; ++H)
+        for (long long grid : {8LL, 12LL, 64LL})
+            if ((fa::xcd_mode_for(H, grid) == fa::kXcdHeads) != (H % 8 == 0) ||
+                (H % 8 != 0 && (fa::xcd_mode_for(H, grid) == fa::kXcdChunks) != (grid % 8 == 0))) {
+                ++bad;
+                printf("xcd_mode_for H=%d grid=%lld\n", H, grid);
+            }
     printf("%ld cases, %ld bad\n", cases, bad);
     return bad != 0;
 }
@@ -76,7 +124,7 @@ int main() {
 
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not found")
-def test_work_item_is_a_bijection_in_heavy_first_order(tmp_path):
+def test_schedule_is_a_bijection_in_heavy_first_order(tmp_path):
     src = tmp_path / "wi.cpp"
     src.write_text(DRIVER)
     exe = tmp_path / "wi"
