@@ -1,7 +1,8 @@
 """The library under a captured HIP graph and from several host threads
 (needs a GPU).
 
-Every entry point allocates nothing, keeps no state and only enqueues on the
+Every entry point (forward, split-KV forward, backward, FP8 forward, row
+softmax) allocates nothing, keeps no state and only enqueues on the
 caller's stream, so (a) a sequence of calls can be captured into a HIP graph
 and replayed, and (b) host threads can call it at the same time on their own
 streams. Both are checked against the same calls made eagerly, bit for bit:
@@ -37,7 +38,7 @@ def _inputs(seed, B=2, H=4, N=300, d=128):
 
 class _Buffers:
     """Preallocated inputs and outputs of one fwd + split-KV fwd + bwd +
-    row-softmax sequence (a graph may not allocate)."""
+    FP8 fwd + row-softmax sequence (a graph may not allocate)."""
 
     def __init__(self, B=2, H=4, N=300, d=128):
         x, self.w = _inputs(1, B, H, N, d)
@@ -53,6 +54,11 @@ class _Buffers:
         self.dout = W.generate_dout(self.w).to(DEV)
         self.grads = tuple(torch.empty(shape, dtype=dt, device=DEV) for _ in range(3))
         self.bws = torch.empty(capi.fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=DEV)
+        self.w8 = W.FP8_BY_NAME["fp8_causal_n8192_d128"].with_shape(B=B, H=H, N=N, d=d, seed=1)
+        x8 = W.generate(self.w8)
+        self.q8, self.k8, self.v8 = (x8[n].to(DEV).clone() for n in ("q", "k", "v"))
+        self.o8 = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        self.lse8 = torch.empty_like(self.lse)
         self.sx = torch.randn(64, 1000, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
         self.sy = torch.empty_like(self.sx)
         self.slse = torch.empty(64, dtype=torch.float32, device=DEV)
@@ -62,6 +68,9 @@ class _Buffers:
         self.q.copy_(x["q"])
         self.k.copy_(x["k"])
         self.v.copy_(x["v"])
+        x8 = W.generate(self.w8.with_shape(seed=seed))
+        for dst, n in ((self.q8, "q"), (self.k8, "k"), (self.v8, "v")):
+            dst.copy_(x8[n])
 
     def run(self):
         sc = self.w.scale
@@ -70,10 +79,14 @@ class _Buffers:
                         num_splits=self.splits, workspace=self.ws)
         A.attention_bwd(self.q, self.k, self.v, self.o, self.dout, self.lse, scale=sc, causal=True,
                         workspace=self.bws, out=self.grads)
+        dq, dk, dv = self.w8.descale
+        A.attention_fwd_fp8(self.q8, self.k8, self.v8, scale=self.w8.scale, descale_q=dq, descale_k=dk,
+                            descale_v=dv, causal=True, out=self.o8, lse=self.lse8)
         S.softmax_rows(self.sx, out=self.sy, lse=self.slse)
 
     def outputs(self):
-        return [t.detach().clone() for t in (self.o, self.lse, self.o2, self.lse2, *self.grads, self.sy, self.slse)]
+        return [t.detach().clone() for t in (self.o, self.lse, self.o2, self.lse2, *self.grads, self.o8, self.lse8,
+                                             self.sy, self.slse)]
 
 
 def test_graph_replays_match_eager():
