@@ -23,9 +23,9 @@
 //     operand (the forward's P V step with K in place of V).
 //   attn_bwd_dkdv_kernel  one workgroup per key tile, walking the query
 //     tiles: V of the wave's 32 keys stays in registers and K in LDS (loaded
-//     once), Q, dO and the tile's (lse2, D) stream through LDS; S = Q K^T and dP = dO V^T with one
-//     key per lane, dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
-//     by the transpose loads.
+//     once), Q, dO and the tile's (lse2, D) stream through LDS; S = Q K^T and
+//     dP = dO V^T with one key per lane, dV^T += dO^T P and dK^T += Q^T dS
+//     with dO^T and Q^T read by the transpose loads.
 //
 // No atomics: each gradient element is accumulated by exactly one lane in
 // fp32 registers and stored once, so results are deterministic. P and dS are
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
     const int col = lane & 31;
     const int hh = lane >> 5;
 
-    int split, bh, qt;
+    int split, bh, qt;  // workgroup -> (one key range, batch*head, query tile), as in the forward
     schedule(blockIdx.x, gridDim.x, p.n_qtiles, p.B * p.H, 1, p.head_group, p.xcd_remap, &split, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
     const int col = lane & 31;
     const int hh = lane >> 5;
 
-    int split, bh, qt;
+    int split, bh, qt;  // workgroup -> (one key range, batch*head, query tile), as in the forward
     schedule(blockIdx.x, gridDim.x, p.n_qtiles, p.B * p.H, 1, p.head_group, p.xcd_remap, &split, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;

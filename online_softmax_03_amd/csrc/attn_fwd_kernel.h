@@ -85,10 +85,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     const int col = lane & 31;  // query within the wave's 32
     const int hh = lane >> 5;   // which 16 of every 32 keys this lane holds
 
-    // workgroup -> (batch*head, query tile). Query tiles of one head are walked
-    // from the last (largest causal extent) to the first, and with the remap
-    // consecutive ids of one XCD (ids are dealt round-robin over 8 XCDs) cover
-    // consecutive tiles, so the workgroups sharing a head's K/V share an L2.
+    // workgroup -> (key-range part, batch*head, query tile): every tile of a
+    // head runs on one XCD, so the workgroups sharing its K/V share an L2, and
+    // each XCD starts its longest tiles (largest causal extent) first
+    // (schedule, work_item.h).
     int split, bh, qt;
     schedule(blockIdx.x, gridDim.x, p.n_qtiles, p.B * p.H, SPLIT ? p.n_splits : 1, p.head_group, p.xcd_remap,
              &split, &bh, &qt);
