@@ -16,7 +16,6 @@ the extra 2^-10 sum p|v| covering float32 accumulation over up to 2^13 keys.
 LSE is formed from the unrounded sum: |dLSE| <= 1e-3. Fully masked rows are
 O = 0 and LSE = -inf exactly. O and LSE are pre-filled with NaN.
 """
-import math
 
 import numpy as np
 import pytest
