@@ -62,10 +62,10 @@ def attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: floa
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, H, N, d] tensor of out_dtype")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous [B, H, N] float32 tensor")
+    if out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous [B, H, N, d] tensor of out_dtype on q's device")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous [B, H, N] float32 tensor on q's device")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     if num_splits is not None:
         if tile is not None:
@@ -128,10 +128,10 @@ def attention_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: 
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, H, N, d] tensor of out_dtype")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous [B, H, N] float32 tensor")
+    if out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous [B, H, N, d] tensor of out_dtype on q's device")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous [B, H, N] float32 tensor on q's device")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = capi.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
                          float(scale), float(descale_q), float(descale_k), float(descale_v), int(bool(causal)),
@@ -174,6 +174,8 @@ def attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     need = capi.fa_bwd_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous buffer on the same device")
     if out is None:
         dq, dk, dv = (torch.empty(q.shape, dtype=grad_dtype, device=q.device) for _ in range(3))
     else:
