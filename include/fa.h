@@ -143,9 +143,9 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
 /* fa_splitkv_num_splits — a split count for these sizes: the smallest count
  * whose workgroups fill every slot of the 256 compute units at once (3
  * resident workgroups per CU for the 16-bit d = 128 kernel, 2 for d = 64 and
- * fp32 inputs), capped so that every part keeps at least four key tiles and
- * at 8 parts. Returns the count (1..8) or a negative fa_status. Host only, no
- * HIP call. */
+ * fp32 inputs), capped so that every part keeps at least four key tiles (one
+ * for fp32 inputs) and at 8 parts. Returns the count (1..8) or a negative
+ * fa_status. Host only, no HIP call. */
 int fa_splitkv_num_splits(int B, int H, int N, int d, int in_dtype);
 
 /*

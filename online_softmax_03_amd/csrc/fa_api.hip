@@ -204,10 +204,13 @@ int fa_splitkv_num_splits(int B, int H, int N, int d, int in_dtype) {
     // keeping at least four key tiles per part and at most 8 parts (beyond
     // that the merge, which reads every part's row, costs more than the
     // extra parallelism gains: 1 x 1 x 8192 runs 287 TFLOP/s at 8 parts and
-    // 270 at 12).
+    // 270 at 12). fp32 tiles run on the fp32 MFMA, many times slower per
+    // tile, so one tile per part already outweighs the merge (the 1 x 1 x
+    // 256 fp32 launch: 24 us unsplit, 16 us in 4 parts).
     const long long slots = 256LL * resident_wgs_per_cu(d, in_dtype);
+    const long long min_tiles = in_dtype == FA_DTYPE_F32 ? 1 : 4;
     long long s = 1;
-    while (s < 8 && grid * s < slots && key_tiles / (s + 1) >= 4) ++s;
+    while (s < 8 && grid * s < slots && key_tiles / (s + 1) >= min_tiles) ++s;
     return (int)s;
 }
 

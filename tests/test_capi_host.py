@@ -122,6 +122,9 @@ def test_splitkv_num_splits_heuristic():
         assert grid * s >= slots or s == 8 or tiles // (s + 1) < 4   # and no fewer parts would do
         assert s == 1 or grid * (s - 1) < slots
     assert capi.fa_splitkv_num_splits(1, 1, 64, 128, BF16) == 1  # too few key tiles to split
+    # fp32 inputs (64-key tiles on the fp32 MFMA) split down to one tile per part
+    assert capi.fa_splitkv_num_splits(1, 1, 256, 64, capi.FA_DTYPE_F32) == 4
+    assert capi.fa_splitkv_num_splits(1, 1, 64, 64, capi.FA_DTYPE_F32) == 1
     assert capi.fa_splitkv_num_splits(1, 1, 0, 128, BF16) == capi.FA_ERR_SHAPE
     assert capi.fa_splitkv_num_splits(1, 1, 64, 80, BF16) == capi.FA_ERR_HEADDIM
     assert capi.fa_splitkv_num_splits(1, 1, 64, 64, 9) == capi.FA_ERR_DTYPE
