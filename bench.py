@@ -5,7 +5,11 @@
 
 A step is one attention forward (one fa_fwd call) over the whole workload,
 inputs already resident in HBM. Prints ONE JSON line. The default workload is
-bf16, causal, d=128, N=8192, B=2, H=32.
+bf16, causal, d=128, N=8192, B=2, H=32. The defaults (100 warm-up steps, 200
+timed) measure the sustained rate: launches right after the GPU leaves idle
+run several per cent slower until its clocks settle (on the default
+workload, 20 timed launches after 5 warm-ups average about 5% below 200
+after 100).
 
 --bwd times the backward (one fa_bwd call per step: the D/LSE pass, the
 dK/dV kernel and the dQ kernel) on the forward's output, with nominal
@@ -49,8 +53,8 @@ KERNEL_PREFIX = "attn_fwd_kernel"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--tile", default=None, help="block_r,block_c")
     ap.add_argument("--shape", default=None, help="B,H,N")
