@@ -112,12 +112,13 @@ def cpu_baseline(w, x, target_s):
 
     run(64)                      # loads the oracle library and warms the caches
     dt, fl, n = run(2048)        # calibration sample
-    # grow the sample until it takes about target_s (larger samples run at a
-    # better rate on many cores, so one extrapolation undershoots)
-    for _ in range(3):
+    # grow the sample until it takes about target_s, at most 4x per step: the
+    # rate per row changes with the sample size (thread use, per-head setup),
+    # so one long extrapolation can land far from the target either way
+    for _ in range(8):
         if dt >= 0.7 * target_s or n >= B * H * N:
             break
-        n = int(min(B * H * N, max(2048, n * target_s / max(dt, 1e-3))))
+        n = int(min(B * H * N, max(2048, n * min(4.0, target_s / max(dt, 1e-3)))))
         dt, fl, n = run(n)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} rows of {w.name} drawn uniformly at random (seed 123), float64 three-pass "
