@@ -275,7 +275,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards over (batch, head) with no exchange; see the design notes)",
+              "(the path would shard over (batch, head) with no exchange: run one process per GPU on its share of the heads)",
               file=sys.stderr)
         sys.exit(2)
 
