@@ -98,9 +98,12 @@ def cpu_baseline(w, x, target_s):
         else:
             oracle.attention(sl(q), sl(k), sl(v), x["scale"], x["causal"], mk, rows=rr, nthreads=threads)
 
-    def run(nrows):
+    def run(nrows, cap=float("inf")):
+        # rows of the sample, head by head; stops after the head that passes
+        # `cap` seconds (all heads are drawn alike, so the rows done so far are
+        # still a uniform sample of query positions)
         rows = np.sort(rng.choice(B * H * N, size=nrows, replace=False))
-        flops = 0.0
+        flops, done = 0.0, 0
         t0 = time.perf_counter()
         for bh in np.unique(rows // N):
             b, h = divmod(int(bh), H)
@@ -108,18 +111,22 @@ def cpu_baseline(w, x, target_s):
             attention(b, h, rr)
             keys = (rr + 1) if w.causal else np.full(rr.shape, N)
             flops += float(4.0 * d * keys.sum())
-        return time.perf_counter() - t0, flops, nrows
+            done += len(rr)
+            if time.perf_counter() - t0 > cap:
+                break
+        return time.perf_counter() - t0, flops, done
 
     run(64)                      # loads the oracle library and warms the caches
     dt, fl, n = run(2048)        # calibration sample
-    # grow the sample until it takes about target_s, at most 4x per step: the
-    # rate per row changes with the sample size (thread use, per-head setup),
-    # so one long extrapolation can land far from the target either way
+    # grow the sample until it takes about target_s, at most 4x per step; the
+    # rate per row is not constant (thread use, per-head setup, a host whose
+    # CPU share shrinks under sustained load), so each run also stops once it
+    # has taken 1.5 * target_s
     for _ in range(8):
         if dt >= 0.7 * target_s or n >= B * H * N:
             break
         n = int(min(B * H * N, max(2048, n * min(4.0, target_s / max(dt, 1e-3)))))
-        dt, fl, n = run(n)
+        dt, fl, n = run(n, cap=1.5 * target_s)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} rows of {w.name} drawn uniformly at random (seed 123), float64 three-pass "
                       f"oracle{' of the decoded E4M3 inputs' if fp8 else ''}, nominal 4*d*(allowed keys) FLOP "
