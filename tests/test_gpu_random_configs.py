@@ -54,10 +54,7 @@ def _draw(i, g):
 FWD = [_draw(i, np.random.default_rng(9000 + i)) for i in range(64)]
 
 
-@pytest.mark.parametrize("i", range(len(FWD)))
-def test_random_forward(i):
-    c = FWD[i]
-    g = np.random.default_rng(9100 + i)
+def _forward(c, g, label):
     w = BASE.with_shape(B=c["B"], H=c["H"], N=c["N"], d=c["d"], in_dtype=c["in_dtype"], out_dtype=c["out_dtype"],
                         causal=c["causal"], seed=c["seed"])
     x = W.generate(w)
@@ -67,18 +64,20 @@ def test_random_forward(i):
     splits = [None, None, 2, 3, 5][int(g.integers(5))]
     if splits is not None:
         tile = None
-    what = f"random forward {i}: {c} tile={tile} splits={splits}"
+    what = f"{label}: {c} tile={tile} splits={splits}"
     U.log(what)
     U.check_full(x, tile=tile, what=what, num_splits=splits)
+
+
+@pytest.mark.parametrize("i", range(len(FWD)))
+def test_random_forward(i):
+    _forward(FWD[i], np.random.default_rng(9100 + i), f"random forward {i}")
 
 
 BWD = [_draw(100 + i, np.random.default_rng(9200 + i)) for i in range(20)]
 
 
-@pytest.mark.parametrize("i", range(len(BWD)))
-def test_random_backward(i):
-    c = BWD[i]
-    g = np.random.default_rng(9300 + i)
+def _backward(c, g, label):
     w = BASE.with_shape(B=c["B"], H=c["H"], N=c["N"], d=c["d"], in_dtype=c["in_dtype"], out_dtype=c["in_dtype"],
                         causal=c["causal"], seed=c["seed"])
     x = W.generate(w)
@@ -86,24 +85,54 @@ def test_random_backward(i):
     do = W.generate_dout(w)
     ref, o, lse = TB._oracle_inputs(x, do)
     grad = [None, "f32"][int(g.integers(2))]
-    U.log(f"random backward {i}: {c} grad={grad}")
+    U.log(f"{label}: {c} grad={grad}")
     got = TB.run_bwd(x, do, o, lse, grad_dtype=grad)
-    TB.check(got, ref, c["in_dtype"], f"random backward {i}")
+    TB.check(got, ref, c["in_dtype"], label)
 
 
-FP8 = [dict(B=int(r.integers(1, 3)), H=int(r.integers(1, 4)), N=int(r.integers(1, 400)), causal=bool(r.integers(2)),
-            mask=str(r.choice(["none", "pad", "general"])), out=str(r.choice(["bf16", "f16", "f32"])),
-            offset=int(r.choice([8, 0])), seed=7000 + i)
-       for i, r in enumerate(np.random.default_rng(9400 + j) for j in range(16))]
+@pytest.mark.parametrize("i", range(len(BWD)))
+def test_random_backward(i):
+    _backward(BWD[i], np.random.default_rng(9300 + i), f"random backward {i}")
 
 
-@pytest.mark.parametrize("i", range(len(FP8)))
-def test_random_fp8(i):
-    c = FP8[i]
-    g = np.random.default_rng(9500 + i)
+def _draw_fp8(i, r):
+    return dict(B=int(r.integers(1, 3)), H=int(r.integers(1, 4)), N=int(r.integers(1, 400)), causal=bool(r.integers(2)),
+                mask=str(r.choice(["none", "pad", "general"])), out=str(r.choice(["bf16", "f16", "f32"])),
+                offset=int(r.choice([8, 0])), seed=7000 + i)
+
+
+FP8 = [_draw_fp8(j, np.random.default_rng(9400 + j)) for j in range(16)]
+
+
+def _fp8(c, g, label):
     w = W.FP8_BY_NAME["fp8_causal_n8192_d128"].with_shape(B=c["B"], H=c["H"], N=c["N"], causal=c["causal"],
                                                         out_dtype=c["out"], seed=c["seed"])
     x = W.generate(w)
     x["mask"], _ = _mask(g, c["mask"], c["B"], c["N"])
-    U.log(f"random fp8 {i}: {c}")
-    T8.check_all_rows(x, c["offset"], f"random fp8 {i}")
+    U.log(f"{label}: {c}")
+    T8.check_all_rows(x, c["offset"], label)
+
+
+@pytest.mark.parametrize("i", range(len(FP8)))
+def test_random_fp8(i):
+    _fp8(FP8[i], np.random.default_rng(9500 + i), f"random fp8 {i}")
+
+
+# A wider sweep from other seeds, in chunks so that each test reports on its
+# own: 16 chunks of 100 forward, 15 backward and 15 FP8 configurations.
+SWEEP_CHUNKS, SWEEP_FWD, SWEEP_BWD, SWEEP_FP8 = 16, 100, 15, 15
+
+
+@pytest.mark.parametrize("k", range(SWEEP_CHUNKS))
+def test_random_sweep_chunk(k):
+    for j in range(SWEEP_FWD):
+        i = k * SWEEP_FWD + j
+        _forward(_draw(i, np.random.default_rng(31000 + i)), np.random.default_rng(41000 + i), f"sweep forward {i}")
+    for j in range(SWEEP_BWD):
+        i = k * SWEEP_BWD + j
+        _backward(_draw(100000 + i, np.random.default_rng(32000 + i)), np.random.default_rng(42000 + i),
+                  f"sweep backward {i}")
+    for j in range(SWEEP_FP8):
+        i = k * SWEEP_FP8 + j
+        _fp8(_draw_fp8(10000 + i, np.random.default_rng(33000 + i)), np.random.default_rng(43000 + i),
+             f"sweep fp8 {i}")
