@@ -138,3 +138,30 @@ def test_full_size_sampled_rows(name):
     sums = y.sum(axis=1)
     rel = Y_TOL[w.out_dtype][0]
     assert np.abs(sums - 1.0).max() <= rel, f"{name}: row sums off by {np.abs(sums - 1).max():.2e}"
+
+
+def _draw_softmax(i):
+    r = np.random.default_rng(15000 + i)
+    pair = PAIRS[int(r.integers(len(PAIRS)))]
+    cols = int(np.exp(r.uniform(0.0, np.log(170000.0))))
+    rows = int(r.integers(1, 12)) if cols <= 20000 else int(r.integers(1, 4))
+    lo = float(r.uniform(-60.0, 0.0))
+    return dict(pair=pair, rows=rows, cols=max(1, cols), masked_frac=float(r.choice([0.0, 0.1, 0.9])),
+                dist=("uniform", lo, lo + float(r.uniform(0.1, 60.0))), seed=16000 + i)
+
+
+SOFTMAX_RANDOM = [_draw_softmax(i) for i in range(120)]
+
+
+@pytest.mark.parametrize("i", range(len(SOFTMAX_RANDOM)))
+def test_random_rows(i):
+    """Seeded random shapes (column counts log-uniform up to 170000, so every
+    kernel form and its boundaries get drawn), dtype pairs, value ranges and
+    masked fractions, every element against the oracle."""
+    c = SOFTMAX_RANDOM[i]
+    w = BASE.with_shape(rows=c["rows"], cols=c["cols"], in_dtype=c["pair"][0], out_dtype=c["pair"][1],
+                        masked_frac=c["masked_frac"], dist=c["dist"], seed=c["seed"])
+    x = W.generate_softmax(w)
+    log(f"case softmax random {i}: {c}")
+    y, lse = run_gpu(x, c["pair"][1])
+    compare(y, lse, x, c["pair"][1], f"softmax random {i}: {c}")
