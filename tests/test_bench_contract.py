@@ -47,3 +47,48 @@ def test_one_json_line_with_roofline_and_cpu_baseline():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0 and cb["cores"] >= 1
     assert "rows of bf16_causal_n8192_d128" in cb["sample"]
+
+
+def test_cpu_baseline_sample_stays_near_its_time_target(monkeypatch):
+    """The oracle baseline's sample sizing, with the oracle replaced by a
+    stand-in whose cost per row rises 16-fold past 20000 rows (a host whose
+    CPU share shrinks under load): the reported sample must still take about
+    the target time, never more than the 1.5x cap plus one head."""
+    import time
+    import types
+
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import bench
+    from online_softmax_03_amd import workloads as W
+
+    done = {"rows": 0}
+
+    def fake_attention(q, k, v, scale, causal, mask, rows=None, nthreads=1):
+        done["rows"] += len(rows)
+        per_row = 2e-6 if done["rows"] < 20000 else 3.2e-5
+        time.sleep(per_row * len(rows))
+
+    fake = types.SimpleNamespace(attention=fake_attention, max_threads=lambda: 4)
+    monkeypatch.setitem(sys.modules, "oracle", fake)
+    w = {x.name: x for x in W.WORKLOADS}["bf16_causal_n8192_d128"]
+    x = {n: torch.zeros(1, dtype=torch.bfloat16) for n in ("q", "k", "v")}
+    x.update(mask=None, scale=0.0884, causal=True)
+
+    class _Arr:
+        def __init__(self):
+            self.shape = (w.B, w.H, w.N, w.d)
+
+        def __getitem__(self, key):
+            return self
+
+    monkeypatch.setattr(torch.Tensor, "float", lambda self: types.SimpleNamespace(numpy=lambda: _Arr()))
+    target = 0.4
+    r = bench.cpu_baseline(w, x, target)
+    seconds = float(r["sample"].rsplit(", ", 1)[1].rstrip(" s"))
+    nrows = int(r["sample"].split(" ", 1)[0])
+    assert 0 < nrows < w.B * w.H * w.N
+    assert 0.7 * target <= seconds <= 1.5 * target + 0.05, r["sample"]
+    assert np.isfinite(r["value"]) and r["value"] > 0
