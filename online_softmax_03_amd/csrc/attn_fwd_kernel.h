@@ -278,6 +278,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
             m_run = m_new;
         }
         const float ref = (m_run == -INFINITY) ? 0.f : m_run * c;
+        // The compiler's exponential/MFMA interleave schedule for the block
+        // below (exponentials, packing, P*V): it spreads the v_exp_f32 and
+        // packing work between the P*V MFMAs instead of ahead of them. Not
+        // with a key mask at d = 128, where it would take some forms past
+        // the 168 registers of three waves per SIMD.
+        if constexpr (!(D == 128 && MASK)) __builtin_amdgcn_iglp_opt(2);
         float rs0 = 0.f, rs1 = 0.f;  // two chains for the fp32 row sum
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
