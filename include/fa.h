@@ -49,7 +49,11 @@ typedef enum {
     FA_DTYPE_F32 = 0,   /* IEEE float32 */
     FA_DTYPE_BF16 = 1,  /* bfloat16 */
     FA_DTYPE_F16 = 2    /* IEEE float16 */
-} fa_dtype;
+} fa_dtype_t;
+
+/* HIP stream handle: the same typedef as <hip/hip_runtime_api.h> makes, so
+ * this header needs no HIP include (C11 and C++ accept the repeated typedef). */
+typedef struct ihipStream_t* hipStream_t;
 
 typedef enum {
     FA_OK = 0,
@@ -96,23 +100,24 @@ typedef struct {
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal,
-           const uint8_t* key_padding_mask, int in_dtype, int out_dtype, void* stream);
+           const uint8_t* key_padding_mask, fa_dtype_t in_dtype, fa_dtype_t out_dtype,
+           hipStream_t stream);
 
 /* fa_fwd_ex — fa_fwd with an explicit tile shape (NULL = default). Returns
  * FA_ERR_TILE if no kernel exists for that shape with these arguments. */
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, float scale, int causal,
-              const uint8_t* key_padding_mask, int in_dtype, int out_dtype, void* stream,
-              const fa_tile* tile);
+              const uint8_t* key_padding_mask, fa_dtype_t in_dtype, fa_dtype_t out_dtype,
+              hipStream_t stream, const fa_tile* tile);
 
 /* fa_default_tile — the tile shape fa_fwd would use for these arguments.
  * Writes *out and returns FA_OK, or returns a negative fa_status. Host only. */
-int fa_default_tile(int N, int d, int in_dtype, int out_dtype, int causal, int has_mask,
-                    fa_tile* out);
+int fa_default_tile(int N, int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype, int causal,
+                    int has_mask, fa_tile* out);
 
 /* fa_tile_supported — FA_OK if fa_fwd_ex accepts `tile` for (d, in_dtype,
  * out_dtype), FA_ERR_TILE otherwise. Host only, no HIP call. */
-int fa_tile_supported(int d, int in_dtype, int out_dtype, const fa_tile* tile);
+int fa_tile_supported(int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype, const fa_tile* tile);
 
 /*
  * Split-KV forward: the keys of every query row are cut into num_splits
@@ -142,11 +147,11 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
 
 /* fa_splitkv_num_splits — a split count for these sizes: the smallest count
  * whose workgroups fill every slot of the 256 compute units at once (3
- * resident workgroups per CU for the 16-bit d = 128 kernel, 2 for d = 64 and
- * fp32 inputs), capped so that every part keeps at least four key tiles (one
+ * resident workgroups per CU for the 16-bit d = 128 kernel, 2 for the 16-bit
+ * d = 64 kernel and fp32 inputs at d = 64, 1 for fp32 inputs at d = 128), capped so that every part keeps at least four key tiles (one
  * for fp32 inputs) and at 8 parts. Returns the count (1..8) or a negative
  * fa_status. Host only, no HIP call. */
-int fa_splitkv_num_splits(int B, int H, int N, int d, int in_dtype);
+int fa_splitkv_num_splits(int B, int H, int N, int d, fa_dtype_t in_dtype);
 
 /*
  * fa_fwd_splitkv — attention forward with the keys split into num_splits
@@ -165,8 +170,8 @@ int fa_splitkv_num_splits(int B, int H, int N, int d, int in_dtype);
  */
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int N, int d, float scale, int causal,
-                   const uint8_t* key_padding_mask, int in_dtype, int out_dtype,
-                   int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+                   const uint8_t* key_padding_mask, fa_dtype_t in_dtype, fa_dtype_t out_dtype,
+                   int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * fa_fwd_fp8 — attention forward with FP8 (OCP E4M3) Q, K, V.
@@ -195,8 +200,8 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, float descale_q, float descale_k,
-               float descale_v, int causal, const uint8_t* key_padding_mask, int out_dtype,
-               int max_offset, void* stream);
+               float descale_v, int causal, const uint8_t* key_padding_mask, fa_dtype_t out_dtype,
+               int max_offset, hipStream_t stream);
 
 /*
  * Attention backward from the saved LSE. The forward keeps no N x N matrix,
@@ -239,8 +244,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N);
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-           float scale, int causal, const uint8_t* key_padding_mask, int in_dtype,
-           int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+           float scale, int causal, const uint8_t* key_padding_mask, fa_dtype_t in_dtype,
+           fa_dtype_t grad_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * fa_softmax_fwd — softmax of every row of a matrix, with the online
@@ -270,7 +275,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * Returns FA_OK or a negative fa_status; nothing is launched on error.
  */
 int fa_softmax_fwd(const void* x, void* y, float* lse, long long rows, int cols,
-                   int in_dtype, int out_dtype, void* stream);
+                   fa_dtype_t in_dtype, fa_dtype_t out_dtype, hipStream_t stream);
 
 /* fa_strerror — a static, human-readable name for a status code. */
 const char* fa_strerror(int status);

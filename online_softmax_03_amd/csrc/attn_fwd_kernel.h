@@ -52,8 +52,19 @@ namespace fa {
 
 // ---------------------------------------------------------------- kernel
 
+// Waves per SIMD the split-KV forms are held to: the host sizes its split
+// count by the workgroups a compute unit holds (resident_wgs_per_cu in
+// fa_api.hip), three for the 128 x 32 tile at d = 128 (at most 168
+// registers). The 256 x 64 tile at d = 64 meets its count of two (at most 128
+// registers) by itself. The other forms carry no bound.
+template <int D, int BC, int NW, bool SPLIT>
+constexpr int min_waves_per_eu() {
+    return (SPLIT && D == 128 && BC == 32 && NW == 4) ? 3 : 1;
+}
+
 template <int D, int BC, int NW, typename TI, typename TO, bool CAUSAL, bool MASK, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<D, BC, NW, SPLIT>())))
+void attn_fwd_kernel(Params p) {
     // The body uses device-only types (buffer resources), so the host pass,
     // which only needs the launch stub, does not see it.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -281,8 +292,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         // The compiler's exponential/MFMA interleave schedule for the block
         // below (exponentials, packing, P*V): it spreads the v_exp_f32 and
         // packing work between the P*V MFMAs instead of ahead of them. Not
-        // with a key mask at d = 128, where it would take some forms past
-        // the 168 registers of three waves per SIMD.
+        // with a key mask at d = 128, where it costs registers (the 64-key
+        // tiles' masked forms grow by 40-50 of them) and gains nothing.
         if constexpr (!(D == 128 && MASK)) __builtin_amdgcn_iglp_opt(2);
         float rs0 = 0.f, rs1 = 0.f;  // two chains for the fp32 row sum
 #pragma unroll

@@ -46,8 +46,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N) {
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-           const uint8_t* key_padding_mask, int in_dtype, int grad_dtype, void* workspace,
-           size_t workspace_bytes, void* stream) {
+           const uint8_t* key_padding_mask, fa_dtype_t in_dtype, fa_dtype_t grad_dtype, void* workspace,
+           size_t workspace_bytes, hipStream_t stream) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
     if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;

@@ -8,6 +8,7 @@
 
 #include "fa.h"
 #include "fa_table.h"
+#include "splitkv_launch.h"
 
 namespace fa {
 extern const EntryList kList_d128_bf16, kList_d128_f16, kList_d64_bf16, kList_d64_f16, kList_f32;
@@ -66,11 +67,15 @@ const fa::MergeEntry* find_merge(int d, int out_dtype) {
     return nullptr;
 }
 
-// Workgroups of the default-tile kernel (plain or split-KV) that one compute
-// unit holds at once (its register use): 3 for the 16-bit d = 128 tile (4
-// waves of at most 168 VGPRs), 2 for the 16-bit d = 64 tile (8 waves of at
-// most 128) and for the fp32 tile.
-int resident_wgs_per_cu(int d, int in_dtype) { return (in_dtype != FA_DTYPE_F32 && d == 128) ? 3 : 2; }
+// Workgroups of the default-tile split-KV kernel that one compute unit holds
+// at once (its register use): 3 for the 16-bit d = 128 tile (4 waves of at
+// most 168 VGPRs, a bound its split forms carry), 2 for the 16-bit d = 64 tile
+// (8 waves of at most 128) and for the fp32 d = 64 tile (4 waves of at most
+// 256), 1 for the fp32 d = 128 tile (4 waves of 256 VGPRs plus AGPRs).
+int resident_wgs_per_cu(int d, int in_dtype) {
+    if (in_dtype == FA_DTYPE_F32) return d == 128 ? 1 : 2;
+    return d == 128 ? 3 : 2;
+}
 
 // Workspace of the split-KV path: fp32 partial outputs [S][B*H*N][d], then
 // their LSEs [S][B*H*N]. 0 if the sizes are out of range.
@@ -125,16 +130,79 @@ fa_tile resolve(int d, int in_dtype, const fa_tile* tile) {
     return t;
 }
 
+
 }  // namespace
+
+namespace fa {
+
+// Argument checks of the split-KV entry points, everything but the
+// workspace (declared in splitkv_launch.h).
+int check_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                  float scale, int in_dtype, int out_dtype, int num_splits) {
+    const int st = check_common(q, k, v, o, lse, B, H, N, d, scale, in_dtype, out_dtype);
+    if (st != FA_OK) return st;
+    if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+    if (splitkv_bytes(B, H, N, d, num_splits) == 0) return FA_ERR_SHAPE;
+    const fa_tile t = default_tile(d, in_dtype);
+    const long long rows = (long long)B * H * N;
+    const long long n_qtiles = ((long long)N + t.block_r - 1) / t.block_r;
+    const long long grid = (long long)B * H * n_qtiles * num_splits;
+    const long long rows_per_block = 256 / (d / 4);
+    const long long merge_grid = (rows + rows_per_block - 1) / rows_per_block;
+    if ((long long)N * d * 4 > INT32_MAX || grid > INT32_MAX || merge_grid > INT32_MAX) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+// The split attention pass and the merge, on a workspace of
+// splitkv_bytes(B, H, N, d, num_splits) bytes at `ws` (arguments already
+// checked by check_splitkv).
+int launch_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, const uint8_t* key_padding_mask, int in_dtype, int out_dtype,
+                   int num_splits, void* ws, hipStream_t s) {
+    const fa_tile t = default_tile(d, in_dtype);
+    const Entry* e = find(d, t, in_dtype, out_dtype, causal, key_padding_mask != nullptr, 1);
+    const fa::MergeEntry* me = find_merge(d, out_dtype);
+    if (!e || !me) return FA_ERR_TILE;
+    const long long rows = (long long)B * H * N;
+    const long long n_qtiles = ((long long)N + t.block_r - 1) / t.block_r;
+    const long long grid = (long long)B * H * n_qtiles * num_splits;
+    const long long rows_per_block = 256 / (d / 4);
+    const long long merge_grid = (rows + rows_per_block - 1) / rows_per_block;
+
+    float* ws_o = static_cast<float*>(ws);
+    float* ws_lse = ws_o + (size_t)num_splits * (size_t)rows * (size_t)d;
+    fa::Params prm;
+    fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, causal, n_qtiles, grid);
+    prm.n_splits = num_splits;
+    prm.ws_o = ws_o;
+    prm.ws_lse = ws_lse;
+    void* args[] = {&prm};
+    if (hipLaunchKernel(e->fn, dim3((unsigned)grid), dim3(e->nwaves * 64), args, 0, s) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    fa::MergeParams mp;
+    mp.ws_o = ws_o;
+    mp.ws_lse = ws_lse;
+    mp.o = o;
+    mp.lse = lse;
+    mp.rows = rows;
+    mp.n_splits = num_splits;
+    void* margs[] = {&mp};
+    if (hipLaunchKernel(me->fn, dim3((unsigned)merge_grid), dim3(256), margs, 0, s) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
+}  // namespace fa
 
 extern "C" {
 
-int fa_tile_supported(int d, int in_dtype, int out_dtype, const fa_tile* tile) {
+int fa_tile_supported(int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype, const fa_tile* tile) {
     const fa_tile t = resolve(d, in_dtype, tile);
     return find(d, t, in_dtype, out_dtype, 0, 0) ? FA_OK : FA_ERR_TILE;
 }
 
-int fa_default_tile(int N, int d, int in_dtype, int out_dtype, int causal, int has_mask, fa_tile* out) {
+int fa_default_tile(int N, int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype, int causal, int has_mask,
+                    fa_tile* out) {
     (void)causal;
     (void)has_mask;
     if (!out) return FA_ERR_NULL;
@@ -146,8 +214,8 @@ int fa_default_tile(int N, int d, int in_dtype, int out_dtype, int causal, int h
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-              int d, float scale, int causal, const uint8_t* key_padding_mask, int in_dtype,
-              int out_dtype, void* stream, const fa_tile* tile) {
+              int d, float scale, int causal, const uint8_t* key_padding_mask, fa_dtype_t in_dtype,
+              fa_dtype_t out_dtype, hipStream_t stream, const fa_tile* tile) {
     const int st = check_common(q, k, v, o, lse, B, H, N, d, scale, in_dtype, out_dtype);
     if (st != FA_OK) return st;
     const fa_tile t = resolve(d, in_dtype, tile);
@@ -183,8 +251,8 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-           float scale, int causal, const uint8_t* key_padding_mask, int in_dtype, int out_dtype,
-           void* stream) {
+           float scale, int causal, const uint8_t* key_padding_mask, fa_dtype_t in_dtype, fa_dtype_t out_dtype,
+           hipStream_t stream) {
     return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask, in_dtype, out_dtype,
                      stream, nullptr);
 }
@@ -193,7 +261,7 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
     return splitkv_bytes(B, H, N, d, num_splits);
 }
 
-int fa_splitkv_num_splits(int B, int H, int N, int d, int in_dtype) {
+int fa_splitkv_num_splits(int B, int H, int N, int d, fa_dtype_t in_dtype) {
     if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
     if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16 && in_dtype != FA_DTYPE_F16) return FA_ERR_DTYPE;
@@ -215,47 +283,15 @@ int fa_splitkv_num_splits(int B, int H, int N, int d, int in_dtype) {
 }
 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-                   int d, float scale, int causal, const uint8_t* key_padding_mask, int in_dtype,
-                   int out_dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-    const int st = check_common(q, k, v, o, lse, B, H, N, d, scale, in_dtype, out_dtype);
+                   int d, float scale, int causal, const uint8_t* key_padding_mask, fa_dtype_t in_dtype,
+                   fa_dtype_t out_dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+    const int st = fa::check_splitkv(q, k, v, o, lse, B, H, N, d, scale, in_dtype, out_dtype, num_splits);
     if (st != FA_OK) return st;
-    if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
     const size_t need = splitkv_bytes(B, H, N, d, num_splits);
-    if (need == 0) return FA_ERR_SHAPE;
     if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FA_ERR_WORKSPACE;
-    const fa_tile t = default_tile(d, in_dtype);
-    const Entry* e = find(d, t, in_dtype, out_dtype, causal, key_padding_mask != nullptr, 1);
-    const fa::MergeEntry* me = find_merge(d, out_dtype);
-    if (!e || !me) return FA_ERR_TILE;
-    const long long rows = (long long)B * H * N;
-    const long long n_qtiles = ((long long)N + t.block_r - 1) / t.block_r;
-    const long long grid = (long long)B * H * n_qtiles * num_splits;
-    const long long rows_per_block = 256 / (d / 4);
-    const long long merge_grid = (rows + rows_per_block - 1) / rows_per_block;
-    if ((long long)N * d * 4 > INT32_MAX || grid > INT32_MAX || merge_grid > INT32_MAX) return FA_ERR_SHAPE;
-
-    float* ws_o = static_cast<float*>(workspace);
-    float* ws_lse = ws_o + (size_t)num_splits * (size_t)rows * (size_t)d;
-    fa::Params prm;
-    fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, causal, n_qtiles, grid);
-    prm.n_splits = num_splits;
-    prm.ws_o = ws_o;
-    prm.ws_lse = ws_lse;
-    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    void* args[] = {&prm};
-    if (hipLaunchKernel(e->fn, dim3((unsigned)grid), dim3(e->nwaves * 64), args, 0, s) != hipSuccess)
-        return FA_ERR_LAUNCH;
-    fa::MergeParams mp;
-    mp.ws_o = ws_o;
-    mp.ws_lse = ws_lse;
-    mp.o = o;
-    mp.lse = lse;
-    mp.rows = rows;
-    mp.n_splits = num_splits;
-    void* margs[] = {&mp};
-    if (hipLaunchKernel(me->fn, dim3((unsigned)merge_grid), dim3(256), margs, 0, s) != hipSuccess)
-        return FA_ERR_LAUNCH;
-    return FA_OK;
+    return fa::launch_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask, in_dtype, out_dtype,
+                          num_splits, workspace, stream);
 }
 
 }  // extern "C"

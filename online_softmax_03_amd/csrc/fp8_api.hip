@@ -18,7 +18,7 @@ extern "C" {
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                float scale, float descale_q, float descale_k, float descale_v, int causal,
-               const uint8_t* key_padding_mask, int out_dtype, int max_offset, void* stream) {
+               const uint8_t* key_padding_mask, fa_dtype_t out_dtype, int max_offset, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
     if (d != 128) return FA_ERR_HEADDIM;

@@ -25,8 +25,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 extern "C" {
 
-int fa_softmax_fwd(const void* x, void* y, float* lse, long long rows, int cols, int in_dtype,
-                   int out_dtype, void* stream) {
+int fa_softmax_fwd(const void* x, void* y, float* lse, long long rows, int cols, fa_dtype_t in_dtype,
+                   fa_dtype_t out_dtype, hipStream_t stream) {
     if (!x || !y) return FA_ERR_NULL;
     if (rows <= 0 || cols <= 0 || rows > INT32_MAX || rows * (long long)cols > (1LL << 40)) return FA_ERR_SHAPE;
     if (!pair_ok(in_dtype, out_dtype)) return FA_ERR_DTYPE;

@@ -18,7 +18,7 @@ Python binding) never does, and the two share no code.
   `softmax_ref.merge_states`: score-level and blocked references used to pin
   the three-pass oracles (and vice versa).
 """
-from .attention import attention, build, load, max_threads  # noqa: F401
+from .attention import attention, build, fully_masked_rows, load, max_threads  # noqa: F401
 from .softmax_rows import softmax_rows  # noqa: F401
 from .attention_bwd import attention_bwd  # noqa: F401
 from . import softmax_ref  # noqa: F401

@@ -125,3 +125,19 @@ def _as_u8(x) -> np.ndarray:
 
 def max_threads() -> int:
     return int(load().oracle_max_threads())
+
+
+def fully_masked_rows(B, H, N, causal=False, mask=None):
+    """The rows with no allowed key, [B][H][N] bool, from the definition of
+    the allowed set alone (no scores): row (b, h, i) attends key j when
+    (not causal or j <= i) and (mask is None or mask[b][j] != 0), and is fully
+    masked when no j qualifies ("Online Softmax 算法详解" sections 7.2-7.3
+    give such rows O = 0 and LSE = -inf)."""
+    if mask is None:
+        valid = np.ones((B, N), dtype=bool)
+    else:
+        valid = _as_u8(mask).reshape(B, N) != 0
+    # number of allowed keys of row i: valid keys among j <= i (causal) or all
+    seen = np.cumsum(valid, axis=1)
+    count = seen if causal else np.repeat(seen[:, -1:], N, axis=1)
+    return np.broadcast_to((count == 0)[:, None, :], (B, H, N)).copy()

@@ -103,32 +103,37 @@ int oracle_attention_rows(const float* q, const float* k, const float* v,
     long long total = (long long)B * H * N;
     if (!rows && nrows != total) return -1;
     int err = 0;
+    int team = 1;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
+    team = omp_get_max_threads();
 #else
     (void)nthreads;
 #endif
-#pragma omp parallel
+    /* one row of scores per thread, allocated before the parallel region so
+     * that every thread of the team reaches the worksharing loop */
+    double* scratch = (double*)malloc(sizeof(double) * (size_t)N * (size_t)team);
+    if (!scratch) return -2;
+#pragma omp parallel num_threads(team)
     {
-        double* s = (double*)malloc(sizeof(double) * (size_t)N);
-        if (!s) {
-#pragma omp atomic write
-            err = -2;
-        } else {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        double* s = scratch + (size_t)tid * (size_t)N;
 #pragma omp for schedule(dynamic, 1)
-            for (long long r = 0; r < nrows; r++) {
-                long long row = rows ? rows[r] : r;
-                if (row < 0 || row >= total) {
+        for (long long r = 0; r < nrows; r++) {
+            long long row = rows ? rows[r] : r;
+            if (row < 0 || row >= total) {
 #pragma omp atomic write
-                    err = -1;
-                    continue;
-                }
-                one_row(q, k, v, mask, B, H, N, d, scale, causal, row, s,
-                        o + r * (long long)d, lse + r, fully_masked + r);
+                err = -1;
+                continue;
             }
-            free(s);
+            one_row(q, k, v, mask, B, H, N, d, scale, causal, row, s,
+                    o + r * (long long)d, lse + r, fully_masked + r);
         }
     }
+    free(scratch);
     return err;
 }
 

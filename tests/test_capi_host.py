@@ -216,3 +216,4 @@ def _fp8(**kw):
 ])
 def test_fp8_invalid_arguments_rejected_on_host(kw, status):
     assert _fp8(**kw) == status
+

@@ -1,8 +1,10 @@
 """Parity of the HIP attention forward with the float64 oracle (needs a GPU).
 
 Small shapes are compared element by element on every row; they span several
-tiles and end in ragged tails. The five full-size workloads are compared on
-sampled rows that the oracle computes one by one. Every run pre-fills O and
+tiles and end in ragged tails. At full size the bf16 d = 64 and fp16
+key-padded workloads are compared on every row; the causal d = 128 ones on
+one row of every 32-row block of every head, which the oracle computes one by
+one, and on the exact fully masked set over every row. Every run pre-fills O and
 LSE with NaN, so an element the kernel fails to write shows up as NaN.
 """
 import math
@@ -106,27 +108,42 @@ def test_worked_examples_as_attention(case, dtype):
     U.check_full(x, what=f"worked example {case} {dtype}")
 
 
-@pytest.mark.parametrize("name", [C2, C3, C4, C5])
-def test_full_size_sampled_rows(name):
+@pytest.mark.parametrize("name", [C2, C5])
+def test_full_size_every_row(name):
+    """The bf16 d = 64 and the fp16 key-padded workloads at full size, every
+    row against the oracle: O and LSE to tolerance, and the fully masked rows
+    (C5's batch of key length 0) exactly, with O = 0 and LSE = -inf there."""
     w = C[name]
-    U.log(f"case {name}: full size B,H,N,d={w.B},{w.H},{w.N},{w.d}")
+    U.log(f"case {name}: full size B,H,N,d={w.B},{w.H},{w.N},{w.d}, every row")
     x = W.generate(w)
-    rows = U.sample_rows(w.B, w.H, w.N, 96, seed=5, causal=w.causal)
-    if w.key_padding:
-        # rows of the batch with no valid key, and of the one with no padding
-        for b in (0, w.B - 1):
-            rows = np.union1d(rows, [(b * w.H) * w.N + i for i in (0, 7, w.N - 1)])
+    U.check_full(x, what=name)
+
+
+@pytest.mark.parametrize("name", [C3, C4])
+def test_full_size_rows_of_every_block(name):
+    """The causal d = 128 workloads at full size. The oracle computes one row
+    of every 32-row block of every head (a block is one wave's share of a
+    query tile; the row within it is drawn at random) plus the first and last
+    rows of a few heads. On every row: no NaN in O or LSE, and LSE = -inf on
+    exactly the oracle's fully masked set (empty under a causal mask without
+    padding: key 0 is allowed to every row)."""
+    w = C[name]
+    U.log(f"case {name}: full size B,H,N,d={w.B},{w.H},{w.N},{w.d}, one row per block")
+    x = W.generate(w)
+    g = np.random.default_rng(17)
+    heads = np.arange(w.B * w.H)
+    blocks = np.arange(0, w.N, 32)
+    per_block = (heads[:, None] * w.N + blocks[None, :] +
+                 g.integers(0, 32, size=(heads.size, blocks.size))).reshape(-1)
+    rows = np.union1d(per_block, U.sample_rows(w.B, w.H, w.N, 96, seed=5, causal=True))
     O, L, _ = U.check_sampled(x, rows, what=name)
     assert not np.isnan(O).any() and not np.isnan(L).any()
-    if w.key_padding:
-        lens = x["lens"].numpy()
-        dead_b = lens == 0
-        assert np.all(np.isneginf(L[dead_b])) and np.all(O[dead_b] == 0)
-        assert not np.isneginf(L[~dead_b]).any()
-    if w.causal:
-        # row 0 of every head attends to key 0 only: O = v_0, LSE = scale*q_0.k_0
-        v0 = x["v"][:, :, 0].double().numpy()
-        assert np.abs(O[:, :, 0] - v0).max() <= U.O_TOL[w.in_dtype]
+    import oracle
+    fm = oracle.fully_masked_rows(w.B, w.H, w.N, w.causal, x["mask"])
+    assert np.array_equal(np.isneginf(L), fm)
+    # row 0 of every head attends to key 0 only: O = v_0
+    v0 = x["v"][:, :, 0].double().numpy()
+    assert np.abs(O[:, :, 0] - v0).max() <= U.O_TOL[w.in_dtype]
 
 
 def test_largest_sequence_at_d128():

@@ -414,3 +414,27 @@ def test_sampled_rows_equal_full_result():
     flatO, flatL, flatF = O.reshape(-1, O.shape[-1]), L.reshape(-1), fm.reshape(-1)
     assert np.array_equal(Or, flatO[rows]) and np.array_equal(fmr, flatF[rows])
     assert np.array_equal(Lr, flatL[rows])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fully_masked_rows_by_brute_force(causal):
+    """The fully-masked set from the allowed-set definition alone matches a
+    brute-force enumeration of every (row, key) pair, and the attention
+    oracle's own flag; masks with holes, empty rows and full rows."""
+    B, H, N = 5, 2, 23
+    g = np.random.default_rng(11)
+    mask = (g.random((B, N)) < 0.3).astype(np.uint8)
+    mask[0] = 0                     # no valid key
+    mask[1] = 1                     # no padding
+    mask[2] = 0
+    mask[2, N - 1] = 1              # only the last key: causal rows < N-1 are empty
+    fm = oracle.fully_masked_rows(B, H, N, causal, mask)
+    brute = np.zeros((B, H, N), dtype=bool)
+    for b in range(B):
+        for i in range(N):
+            brute[b, :, i] = not any((not causal or j <= i) and mask[b, j] != 0 for j in range(N))
+    assert np.array_equal(fm, brute)
+    q = _rand((B, H, N, 4), 81).astype(np.float32)
+    _, L, fm_oracle = oracle.attention(q, q, q, 0.5, causal, mask)
+    assert np.array_equal(fm, fm_oracle) and np.array_equal(np.isneginf(L), fm)
+    assert not oracle.fully_masked_rows(2, 3, 7, causal, None).any()
