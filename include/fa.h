@@ -67,7 +67,8 @@ typedef enum {
     FA_ERR_LAUNCH = -8,    /* the HIP runtime rejected the kernel launch */
     FA_ERR_SPLITS = -9,    /* num_splits outside [1, FA_MAX_SPLITS] */
     FA_ERR_WORKSPACE = -10, /* workspace NULL, not 16-byte aligned, or too small */
-    FA_ERR_OFFSET = -11     /* fa_fwd_fp8: max_offset is neither 0 nor 8 */
+    FA_ERR_OFFSET = -11,    /* fa_fwd_fp8: max_offset is neither 0 nor 8 */
+    FA_ERR_SCRATCH = -12    /* fa_fwd_splitkv_noalloc: the partials exceed FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 /* Largest number of key-range parts fa_fwd_splitkv accepts. */
@@ -172,6 +173,32 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int N, int d, float scale, int causal,
                    const uint8_t* key_padding_mask, fa_dtype_t in_dtype, fa_dtype_t out_dtype,
                    int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the fixed device scratch behind fa_fwd_splitkv_noalloc: 64 MiB per
+ * device (e.g. 8 parts of B*H*N = 8192 rows at d = 128 need 33.8 MB). */
+#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * fa_fwd_splitkv_noalloc — fa_fwd_splitkv without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). The split partials go
+ * to a fixed scratch array of FA_NOALLOC_SCRATCH_BYTES that the library's code
+ * object holds on every device it is loaded on, until the process ends; the
+ * call itself allocates nothing. Arguments and result as fa_fwd_splitkv, on
+ * the calling thread's current device (the device of `stream`).
+ *   Returns FA_ERR_SCRATCH, before any HIP call, when
+ *   fa_splitkv_workspace_bytes(B, H, N, d, num_splits) > FA_NOALLOC_SCRATCH_BYTES
+ *   (use fewer parts, or fa_fwd_splitkv with a workspace), and FA_ERR_LAUNCH
+ *   if the scratch cannot be resolved on the current device.
+ * Every call on a device shares that device's scratch, which keeps the last
+ * call's partials (nothing in it needs to start at zero): calls on one device
+ * must be ordered (same stream, or an event between them); calls that overlap
+ * race and give wrong results.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const uint8_t* key_padding_mask, fa_dtype_t in_dtype,
+                           fa_dtype_t out_dtype, int num_splits, hipStream_t stream);
 
 /*
  * fa_fwd_fp8 — attention forward with FP8 (OCP E4M3) Q, K, V.

@@ -29,12 +29,14 @@ FA_ERR_LAUNCH = -8
 FA_ERR_SPLITS = -9
 FA_ERR_WORKSPACE = -10
 FA_ERR_OFFSET = -11
+FA_ERR_SCRATCH = -12
 
 FA_MAX_SPLITS = 64
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_default_tile", "fa_tile_supported", "fa_splitkv_workspace_bytes",
-           "fa_splitkv_num_splits", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_softmax_fwd",
+           "fa_splitkv_num_splits", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_softmax_fwd",
            "fa_strerror")
 
 
@@ -74,6 +76,8 @@ def library():
             lib.fa_splitkv_num_splits.argtypes = [_I, _I, _I, _I, _I]
             lib.fa_fwd_splitkv.restype = _I
             lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:-1] + [_I, _P, ctypes.c_size_t, _P]
+            lib.fa_fwd_splitkv_noalloc.restype = _I
+            lib.fa_fwd_splitkv_noalloc.argtypes = _FWD_ARGS[:-1] + [_I, _P]
             lib.fa_fwd_fp8.restype = _I
             lib.fa_fwd_fp8.argtypes = ([_P] * 5 + [_I, _I, _I, _I] + [ctypes.c_float] * 4 +
                                        [_I, _P, _I, _I, _P])
@@ -129,6 +133,12 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask,
                    num_splits, workspace, workspace_bytes, stream) -> int:
     return library().fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask,
                                     in_dtype, out_dtype, num_splits, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask, in_dtype, out_dtype,
+                           num_splits, stream) -> int:
+    return library().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask,
+                                            in_dtype, out_dtype, num_splits, stream)
 
 
 def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, descale_q, descale_k, descale_v, causal, key_padding_mask,

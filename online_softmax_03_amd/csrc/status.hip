@@ -19,6 +19,7 @@ const char* fa_strerror(int status) {
         case FA_ERR_SPLITS: return "num_splits must be in [1, FA_MAX_SPLITS]";
         case FA_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned, or too small";
         case FA_ERR_OFFSET: return "max_offset must be 0 or 8";
+        case FA_ERR_SCRATCH: return "split partials exceed the fixed scratch (FA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

@@ -50,7 +50,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["attn_common.h", "work_item.h", "attn_fwd_kernel.h", "attn_fwd_f32_kernel.h", "attn_merge.h",
                         "fa_table.h", "kern_d128_bf16.hip", "kern_d128_f16.hip", "kern_d64_bf16.hip",
-                        "kern_d64_f16.hip", "kern_f32.hip", "kern_merge.hip", "fa_api.hip", "splitkv_launch.h"],
+                        "kern_d64_f16.hip", "kern_f32.hip", "kern_merge.hip", "fa_api.hip", "splitkv_launch.h",
+                        "noalloc_api.hip"],
     "softmax": ["attn_common.h", "work_item.h", "softmax_kernel.h", "softmax_table.h", "kern_softmax.hip", "softmax_api.hip"],
     "attn_fwd_fp8": ["attn_common.h", "work_item.h", "attn_fwd_fp8_kernel.h", "fp8_table.h", "kern_fp8.hip", "fp8_api.hip"],
     "attn_bwd": ["attn_common.h", "work_item.h", "attn_bwd_kernel.h", "bwd_table.h", "kern_bwd_bf16.hip", "kern_bwd_f16.hip",

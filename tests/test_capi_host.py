@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_names_every_status():
-    names = {s: capi.fa_strerror(s) for s in range(-11, 1)}
+    names = {s: capi.fa_strerror(s) for s in range(-12, 1)}
     assert names[0] == "ok"
     assert len(set(names.values())) == len(names)
     assert capi.fa_strerror(-99) == "unknown status"
@@ -217,3 +217,26 @@ def _fp8(**kw):
 def test_fp8_invalid_arguments_rejected_on_host(kw, status):
     assert _fp8(**kw) == status
 
+
+def _noalloc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=128, scale=0.125, causal=0,
+             key_padding_mask=None, in_dtype=BF16, out_dtype=BF16, num_splits=2, stream=None)
+    a.update(kw)
+    return capi.fa_fwd_splitkv_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), capi.FA_ERR_NULL), (dict(o=None), capi.FA_ERR_NULL),
+    (dict(H=0), capi.FA_ERR_SHAPE), (dict(d=80), capi.FA_ERR_HEADDIM),
+    (dict(in_dtype=F16, out_dtype=BF16), capi.FA_ERR_DTYPE), (dict(scale=0.0), capi.FA_ERR_SCALE),
+    (dict(k=P + 4), capi.FA_ERR_ALIGN),
+    (dict(num_splits=0), capi.FA_ERR_SPLITS), (dict(num_splits=capi.FA_MAX_SPLITS + 1), capi.FA_ERR_SPLITS),
+    # partials beyond the fixed scratch: 2 parts of 64 * 8192 rows at d = 128 (541 MB)
+    (dict(H=64, N=8192, num_splits=2), capi.FA_ERR_SCRATCH),
+    # one row past the limit: S * rows * (d + 1) * 4 bytes > 64 MiB
+    (dict(N=(capi.FA_NOALLOC_SCRATCH_BYTES // (129 * 4)) // 2 + 1, num_splits=2), capi.FA_ERR_SCRATCH),
+])
+def test_noalloc_invalid_arguments_rejected_on_host(kw, status):
+    """Every rejection, the size limit of the fixed scratch included, happens
+    before the entry point makes any HIP call."""
+    assert _noalloc(**kw) == status
