@@ -5,11 +5,12 @@
 
 A step is one attention forward (one fa_fwd call) over the whole workload,
 inputs already resident in HBM. Prints ONE JSON line. The default workload is
-bf16, causal, d=128, N=8192, B=2, H=32. The defaults (100 warm-up steps, 200
-timed) measure the sustained rate: launches right after the GPU leaves idle
-run several per cent slower until its clocks settle (on the default
-workload, 20 timed launches after 5 warm-ups average about 5% below 200
-after 100).
+bf16, causal, d=128, N=8192, B=2, H=32. Before the W warm-up steps the step
+runs back to back for --settle-ms (300 ms) so that the GPU has left its idle
+clock, which it takes a few hundred milliseconds of load to do (the first
+ten launches after idle average 1.5 ms, the sustained rate is 1.05 ms); the
+JSON line reports that phase as `settle` and the shader clock sampled during
+the K timed steps as `clock`.
 
 --bwd times the backward (one fa_bwd call per step: the D/LSE pass, the
 dK/dV kernel and the dQ kernel) on the forward's output, with nominal
@@ -53,8 +54,8 @@ KERNEL_PREFIX = "attn_fwd_kernel"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--tile", default=None, help="block_r,block_c")
     ap.add_argument("--shape", default=None, help="B,H,N")
@@ -67,6 +68,9 @@ def parse():
                          "(0: skip); reported as roofline.flushed_*")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before the warm-up steps, run the step back to back for this long so the GPU leaves "
+                         "its idle clock (0: skip); reported as `settle`")
     return ap.parse_args()
 
 
@@ -133,12 +137,12 @@ def cpu_baseline(w, x, target_s):
                       f"per row, {dt:.1f} s"}
 
 
-def traffic(workload, kernel=KERNEL_PREFIX):
+def traffic(workload, kernel=KERNEL_PREFIX, tile=None):
     """(HBM bytes per launch, detail) from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, when it was taken on the current kernel sources; else
-    (None, None)."""
+    WRITE_SIZE summary, when it was taken on the current kernel sources and
+    the same tile shape; else (None, None)."""
     from online_softmax_03_amd import profiling
-    t = profiling.current_traffic(workload, kernel)
+    t = profiling.current_traffic(workload, kernel, tile)
     if t is None:
         return None, None
     return round(t["hbm_bytes_per_launch"]), {
@@ -147,9 +151,82 @@ def traffic(workload, kernel=KERNEL_PREFIX):
         "source": os.path.relpath(profiling.traffic_file(workload, kernel), ROOT)}
 
 
-def timed_steps(step, stream, steps, warmup):
+class ClockSampler:
+    """Samples the GPU's current shader clock (MHz) from the SMU through
+    amdsmi (else rocm-smi) in a background thread while `active`; reports
+    the median of the samples taken. The SMU figure is an average over its
+    own short window, so it is a reading of the clock, not a cycle count."""
+
+    def __init__(self, period_s=0.002):
+        self.period_s = period_s
+        self.samples = []
+        self.active = False
+        self.source = None
+        self._stop = False
+        self._read = self._open()
+        self._thread = None
+        if self._read is not None:
+            import threading
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+
+    def _open(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handle = amdsmi.amdsmi_get_processor_handles()[0]
+            gfx = amdsmi.AmdSmiClkType.GFX
+            amdsmi.amdsmi_get_clock_info(handle, gfx)
+            self.source = "amdsmi_get_clock_info(GFX).clk"
+            return lambda: float(amdsmi.amdsmi_get_clock_info(handle, gfx)["clk"])
+        except Exception:
+            return None
+
+    def _loop(self):
+        while not self._stop:
+            if self.active:
+                try:
+                    self.samples.append(self._read())
+                except Exception:
+                    pass
+            time.sleep(self.period_s)
+
+    def close(self):
+        self._stop = True
+        if self._thread is not None:
+            self._thread.join()
+
+    def report(self):
+        if not self.samples:
+            return None
+        return {"median_mhz": _median(self.samples), "min_mhz": min(self.samples), "max_mhz": max(self.samples),
+                "samples": len(self.samples), "source": self.source}
+
+
+def settle(step, settle_ms):
+    """Runs `step` back to back for `settle_ms` of wall time (at least once),
+    then synchronises; returns the number of steps run. After idle the GPU
+    starts its clock at a few hundred MHz and takes a few hundred
+    milliseconds of load to reach its working clock; the first ten 1 ms
+    launches of the default workload average 1.5 ms, the next ones 1.05."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= settle_ms:
+                break
+    torch.cuda.synchronize()
+    return n
+
+
+def timed_steps(step, stream, steps, warmup, clock=None):
     """Runs `warmup` untimed steps, then `steps` timed ones with a HIP event
-    pair around each on `stream`. Returns (wall seconds, per-launch ms list)."""
+    pair around each on `stream`. Returns (wall seconds, per-launch ms list).
+    `clock` (a ClockSampler) samples during the timed steps."""
     import torch
     for _ in range(warmup):
         step()
@@ -157,6 +234,8 @@ def timed_steps(step, stream, steps, warmup):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
+    if clock is not None:
+        clock.active = True
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
@@ -164,6 +243,8 @@ def timed_steps(step, stream, steps, warmup):
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if clock is not None:
+        clock.active = False
     return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
@@ -238,7 +319,10 @@ def bench_softmax(args):
     def step():
         S.softmax_rows(xd, out_dtype=y.dtype, out=y, lse=lse)
 
-    wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup)
+    settled = settle(step, args.settle_ms) if args.settle_ms > 0 else 0
+    clock = ClockSampler()
+    wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup, clock)
+    clock.close()
     avg_s = sum(launch_ms) / len(launch_ms) / 1e3
     nbytes = w.algorithmic_bytes()
     # the library's choice: registers (up to 8192 16-byte vectors), registers
@@ -272,6 +356,8 @@ def bench_softmax(args):
                      "traffic": hbm_bytes, "traffic_detail": hbm_detail, "kernel": kernel,
                      "avg_launch_ms": round(avg_s * 1e3, 4),
                      "min_launch_ms": round(min(launch_ms), 4)},
+        "clock": clock.report(),
+        "settle": {"ms": args.settle_ms, "steps": settled},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = softmax_cpu_baseline(w, x, args.cpu_seconds)
@@ -350,8 +436,12 @@ def main():
             A.attention_fwd(q, k, v, scale=w.scale, causal=w.causal, key_padding_mask=mask,
                             out_dtype=out_dt, out=o, lse=lse, num_splits=splits, workspace=ws)
 
-    # per-launch HIP events on the stream the kernel is launched on
-    wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup)
+    # the GPU leaves its idle clock first; then per-launch HIP events on the
+    # stream the kernel is launched on, with the shader clock sampled alongside
+    settled = settle(step, args.settle_ms) if args.settle_ms > 0 else 0
+    clock = ClockSampler()
+    wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup, clock)
+    clock.close()
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     flushed = flushed_launches(step, stream, 5, args.flush_mib) if args.flush_mib > 0 else None
 
@@ -370,7 +460,11 @@ def main():
                      "fraction_of_nominal": round(eff_flops / flops, 4)}
     peak = PEAK_TFLOPS[w.in_dtype]
     kernel = "attn_fwd_fp8_kernel" if fp8 else KERNEL_PREFIX
-    hbm_bytes, hbm_detail = traffic(w.name, kernel) if (splits is None and not args.bwd) else (None, None)
+    hbm_bytes, hbm_detail = (traffic(w.name, kernel, None if fp8 else tile) if (splits is None and not args.bwd)
+                             else (None, None))
+    # the roofline credits only the allowed (query, key) pairs: padded keys
+    # are work the kernel skips, not work it does
+    credited = effective["flops_per_step"] if effective else flops
     result = {
         "metric": ("attention bwd TFLOP/s (nominal 2.5x the forward's FLOPs) and % of MFMA bf16 peak"
                    if args.bwd else
@@ -394,14 +488,19 @@ def main():
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         **({"effective": effective} if effective else {}),
         **({"max_offset": args.max_offset, "descale": list(w.descale)} if fp8 else {}),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": hbm_bytes, "traffic_detail": hbm_detail,
+        "roofline": {"bound": "mfma", "achieved": round(credited / avg_launch_s / 1e12, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(credited / avg_launch_s / 1e12 / peak, 4),
+                     **({"nominal_achieved": round(achieved, 2), "nominal_frac": round(achieved / peak, 4),
+                         "credited": "allowed (query, key) pairs"} if effective else {}),
+                     "traffic": hbm_bytes, "traffic_detail": hbm_detail,
                      "kernel": "attn_bwd (prep + dkdv + dq)" if args.bwd else kernel,
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4),
                      "median_launch_ms": round(_median(launch_ms), 4),
                      "min_launch_ms": round(min(launch_ms), 4),
                      **({"flushed_mib": args.flush_mib, "flushed_median_launch_ms": round(_median(flushed), 4),
                          "flushed_min_launch_ms": round(min(flushed), 4)} if flushed else {})},
+        "clock": clock.report(),
+        "settle": {"ms": args.settle_ms, "steps": settled},
     }
     if not args.no_cpu_baseline and not args.bwd:
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

@@ -48,7 +48,12 @@ extern "C" {
 typedef enum {
     FA_DTYPE_F32 = 0,   /* IEEE float32 */
     FA_DTYPE_BF16 = 1,  /* bfloat16 */
-    FA_DTYPE_F16 = 2    /* IEEE float16 */
+    FA_DTYPE_F16 = 2,   /* IEEE float16 */
+    /* Not dtypes: these give the enum the range of a 32-bit int, so every
+     * int a caller passes is a value the library may read and reject with
+     * FA_ERR_DTYPE. */
+    FA_DTYPE_RANGE_MIN_ = INT32_MIN,
+    FA_DTYPE_RANGE_MAX_ = INT32_MAX
 } fa_dtype_t;
 
 /* HIP stream handle: the same typedef as <hip/hip_runtime_api.h> makes, so

@@ -219,14 +219,15 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
     const int st = check_common(q, k, v, o, lse, B, H, N, d, scale, in_dtype, out_dtype);
     if (st != FA_OK) return st;
     const fa_tile t = resolve(d, in_dtype, tile);
-    const Entry* e = find(d, t, in_dtype, out_dtype, causal, key_padding_mask != nullptr);
-    if (!e) return FA_ERR_TILE;
+    if (t.block_r <= 0 || t.block_r % 32 != 0) return FA_ERR_TILE;
     // Sizes: every byte offset is computed in 64 bits on the device, but a
     // row index times the row size must fit in 32 bits, and so must the grid.
     const long long rows = (long long)B * H * N;
     const long long n_qtiles = ((long long)N + t.block_r - 1) / t.block_r;
     const long long grid = (long long)B * H * n_qtiles;
     if (rows > (1LL << 40) || (long long)N * d * 4 > INT32_MAX || grid > INT32_MAX) return FA_ERR_SHAPE;
+    const Entry* e = find(d, t, in_dtype, out_dtype, causal, key_padding_mask != nullptr);
+    if (!e) return FA_ERR_TILE;
 
     fa::Params prm;
     fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, causal, n_qtiles, grid);

@@ -28,6 +28,10 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     if (max_offset != 0 && max_offset != 8) return FA_ERR_OFFSET;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return FA_ERR_ALIGN;
+    const long long rows = (long long)B * H * N;
+    const long long n_qtiles = ((long long)N + fa::kFp8NW * 32 - 1) / (fa::kFp8NW * 32);
+    const long long grid = (long long)B * H * n_qtiles;
+    if (rows > (1LL << 40) || (long long)N * d * 4 > INT32_MAX || grid > INT32_MAX) return FA_ERR_SHAPE;
     const fa::Fp8Entry* e = nullptr;
     for (int i = 0; i < fa::kFp8Count; ++i) {
         const fa::Fp8Entry& x = fa::kFp8[i];
@@ -36,10 +40,6 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
             e = &x;
     }
     if (!e) return FA_ERR_DTYPE;
-    const long long rows = (long long)B * H * N;
-    const long long n_qtiles = ((long long)N + fa::kFp8NW * 32 - 1) / (fa::kFp8NW * 32);
-    const long long grid = (long long)B * H * n_qtiles;
-    if (rows > (1LL << 40) || (long long)N * d * 4 > INT32_MAX || grid > INT32_MAX) return FA_ERR_SHAPE;
     fa::ParamsFp8 prm;
     prm.q = q;
     prm.k = k;

@@ -78,15 +78,20 @@ def traffic_file(workload: str, kernel: str = "attn_fwd_kernel") -> str:
     return os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
 
 
-def current_traffic(workload: str, kernel: str = "attn_fwd_kernel"):
-    """The measured traffic summary for `workload` if it matches the current
-    kernel sources, else None."""
+def current_traffic(workload: str, kernel: str = "attn_fwd_kernel", tile=None):
+    """The measured traffic summary for `workload` if it was taken on the
+    current kernel sources and on the same tile shape (`tile` = (B_r, B_c),
+    or None where the kernel has one shape), else None."""
     path = traffic_file(workload, kernel)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    return t if t.get("source_hash") == source_hash(_family(kernel)) else None
+    if t.get("source_hash") != source_hash(_family(kernel)):
+        return None
+    if tile is not None and tuple(t.get("tile") or ()) != tuple(tile):
+        return None
+    return t
 
 
 def _family(kernel: str) -> str:
@@ -140,6 +145,7 @@ def _summarize(a) -> None:
     out = {
         "workload": a.workload,
         "kernel": a.kernel,
+        "tile": [int(t) for t in a.tile.split(",")] if a.tile else None,
         "source_hash": source_hash(_family(a.kernel)),
         "dispatches": {"fetch": len(fetch), "write": len(write)},
         "fetch_kib_per_dispatch_raw": fetch_kib,
@@ -290,6 +296,7 @@ def main():
     s = sub.add_parser("summarize")
     s.add_argument("--workload", required=True)
     s.add_argument("--kernel", default="attn_fwd_kernel")
+    s.add_argument("--tile", default=None, help="B_r,B_c of the profiled launch")
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
     s.add_argument("--copy-fetch", required=True)

@@ -47,6 +47,20 @@ def test_one_json_line_with_roofline_and_cpu_baseline():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0 and cb["cores"] >= 1
     assert "rows of bf16_causal_n8192_d128" in cb["sample"]
+    assert d["settle"]["steps"] >= 1
+    assert d["clock"] is None or 100 <= d["clock"]["median_mhz"] <= 2500
+
+
+@pytest.mark.gpu
+def test_key_padded_roofline_credits_allowed_pairs_only():
+    r = _bench("--workload", "f16_keypad_n4096_d64", "--steps", "3", "--warmup", "1", "--flush-mib", "0",
+               "--settle-ms", "0", "--no-cpu-baseline")
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    rf, eff = d["roofline"], d["effective"]
+    assert rf["achieved"] == pytest.approx(eff["tflops"], rel=1e-3)
+    assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], rel=1e-3)
+    assert rf["nominal_frac"] > rf["frac"] and 0 < eff["fraction_of_nominal"] < 1
 
 
 def test_cpu_baseline_sample_stays_near_its_time_target(monkeypatch):
