@@ -17,9 +17,13 @@
 //     of P into E4M3's normal range. The running sum l' is taken from the
 //     float32 P' and compensated at the end, l = l' / 2^MAXOFF, so the LSE is
 //     unchanged; O = acc / l' needs no further factor because acc carries the
-//     same 2^MAXOFF. The rescale margin is 0.5 (log2 units) instead of 8: P'
-//     must stay below 464, where the E4M3 conversion overflows, and
-//     256 * 2^0.5 = 362.
+//     same 2^MAXOFF. P' must stay at most 448, E4M3's largest value, so a
+//     growing row maximum cannot be left in P' for long (2^0.8 at most). The
+//     growth goes instead into the instruction's E8M0 block scale of the P
+//     operand, a per-lane power of two: O and the row sum keep a fixed
+//     reference and are never multiplied on the way (see the online update
+//     below); the 16-bit kernel's rescale of O by alpha is left for growth
+//     beyond 2^64.
 //   * V^T, the A operand of the P V product, is read from the row-major V
 //     tile with ds_read_b64_tr_b8: within each 16-lane group, output byte b of
 //     lane j is element j%8 of the 8-byte chunk addressed by lane 2b + j/8
@@ -53,13 +57,19 @@ struct ParamsFp8 {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-// Largest growth of a row maximum (log2 units) before the state is
-// rescaled on the FP8 path: 2^(8 + 0.5) = 362 < 464.
-constexpr float kRescaleLog2Fp8 = 0.5f;
+// Growth of the running maximum above the frame (log2 units) that P'' may
+// carry before the next power of two moves into the block scale: P'' stays
+// at most 2^(8 + 0.8) = 446, below E4M3's largest value 448.
+constexpr float kFp8Headroom = 0.8f;
+// Largest block-scale exponent before the frame itself moves: O and the row
+// sum then hold at most 2^(64 + 8.8) times a sum of |V| rows, far inside fp32.
+constexpr int kFp8MaxShift = 64;
 
-__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
-    // format 0 = E4M3 for both operands; block scales 127 = 2^0
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// E4M3 x E4M3 -> float32, 32x32x64. The block scales are E8M0 (2^(e - 127)),
+// one per lane for the 32 contraction elements the lane holds; A's are 2^0 and
+// B's `scale_b` (one value per lane).
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c, int scale_b = 127) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, scale_b);
 }
 
 template <int D, int NW, typename TO, bool CAUSAL, bool MASK, int MAXOFF>
@@ -172,8 +182,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-    float m_run = -INFINITY;
-    float l_run = 0.f;       // this lane's share of the running sum of P' = 2^MAXOFF P
+    float m_run = -INFINITY;  // running row maximum, raw q.k units
+    float frame = -INFINITY;  // reference of acc and l_run, log2 units
+    float l_run = 0.f;        // this lane's share of the running sum of 2^(s*c - frame + MAXOFF)
     const float c = p.c;
     const bool wave_live = qw0 < N;
     const int qq = qw0 + col;
@@ -240,23 +251,37 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
             }
         }
 
-        // ---- online update with the FP8 offset
+        // ---- online update with the FP8 offset. The accumulators stay in a
+        // fixed frame F (log2 units: the first maximum the row sees), and the
+        // growth of the running maximum above it, g = M*c - F, is split into
+        // an integer k = max(0, ceil(g - kFp8Headroom)) and the rest: P is
+        // formed as P'' = 2^(s*c - F - k + MAXOFF), at most 2^(MAXOFF +
+        // headroom), and the factor 2^k is applied by the P V instruction's
+        // E8M0 block scale of the P operand (lane l's scale covers its query's
+        // 32 keys) and to the row sum by ldexp, exactly. The frame moves (a
+        // rescale of O and l by 2^-k) only when k would pass kFp8MaxShift.
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         mx = pair_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kRescaleLog2Fp8) != 0) {
-            const float alpha =
-                __builtin_amdgcn_exp2f(m_run * c - ((m_new == -INFINITY) ? 0.f : m_new * c));
-            l_run *= alpha;
+        m_run = fmaxf(m_run, mx);
+        const float mc = m_run * c;                  // -inf while the row has no allowed key
+        if (frame == -INFINITY) frame = mc;          // the first key the row sees sets the frame
+        const float g = mc - frame;                  // NaN while both are -inf
+        int k = g > kFp8Headroom ? (int)__builtin_ceilf(g - kFp8Headroom) : 0;
+        if (__builtin_amdgcn_ballot_w64(k > kFp8MaxShift) != 0) {
+            // move the frame up by k: O and l scale by 2^-k, exactly
+            l_run = __builtin_ldexpf(l_run, -k);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-            m_run = m_new;
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[db][r] = __builtin_ldexpf(acc[db][r], -k);
+            frame += (float)k;
+            k = 0;
         }
-        const float ref = ((m_run == -INFINITY) ? 0.f : m_run * c) - (float)MAXOFF;
+        const float ref = ((frame == -INFINITY) ? 0.f : frame + (float)k) - (float)MAXOFF;
         float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -266,7 +291,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
                 if (r & 1) rs1 += s[kb][r];
                 else rs0 += s[kb][r];
             }
-        l_run += rs0 + rs1;
+        l_run += __builtin_ldexpf(rs0 + rs1, k);
+        const int pscale = 127 + k;  // E8M0 2^k
 
         // ---- P'^T as E4M3: byte 16*kb + r holds register r of block kb. The
         // first conversion of a word writes its low half and keeps the high
@@ -292,7 +318,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
                 a[2 * t] = r2[0];
                 a[2 * t + 1] = r2[1];
             }
-            acc[db] = mfma_fp8(a, pb, acc[db]);
+            acc[db] = mfma_fp8(a, pb, acc[db], pscale);
         }
     };
 
@@ -309,11 +335,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
         compute_tile(it + 1, buf1);
     }
 
-    // ---- finalize: l = l' / 2^MAXOFF for the LSE; O = acc / l' * descale_v
+    // ---- finalize: l = l' / 2^MAXOFF in the frame's units for the LSE;
+    // O = acc / l' * descale_v
     const float l_tot = pair_sum(l_run);
     const bool dead = !(l_tot > 0.f);
     const float inv = dead ? 0.f : p.descale_v / l_tot;
-    const float lse = dead ? -INFINITY : (m_run * c + __builtin_amdgcn_logf(l_tot) - (float)MAXOFF) * kLn2;
+    const float lse = dead ? -INFINITY : (frame + __builtin_amdgcn_logf(l_tot) - (float)MAXOFF) * kLn2;
     if (qq < N) {
         char* orow = reinterpret_cast<char*>(p.o) + (head + (size_t)qq * D) * TO::kBytes;
 #pragma unroll
