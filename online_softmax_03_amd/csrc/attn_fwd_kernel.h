@@ -36,9 +36,11 @@
 //      group, and the V^T operand is read from the row-major V tile with
 //      ds_read_b64_tr_b16 in that same key order. No LDS round trip for P.
 //      The row sum l is accumulated from the fp32 P before rounding (as the
-//      deferred row sum of "Online Softmax 算法详解" section 4.6 is): summing
-//      the rounded values instead would put bf16's 2^-9 relative error
-//      straight into the LSE.
+//      deferred row sum of "Online Softmax 算法详解" section 4.6 is) for bf16
+//      inputs: summing the rounded values instead would put bf16's 2^-9
+//      relative error straight into the LSE. For fp16 inputs it is taken from
+//      the rounded P (2^-11 relative, an LSE error of at most 4.9e-4), two
+//      values per v_dot2_f32_f16.
 //
 // After the last tile: the two lane halves' row sums are added (the deferred
 // cross-lane reduce of "Online Softmax 算法详解" section 4.6), inv = 1/l with the
@@ -295,16 +297,18 @@ void attn_fwd_kernel(Params p) {
         // with a key mask at d = 128, where it costs registers (the 64-key
         // tiles' masked forms grow by 40-50 of them) and gains nothing.
         if constexpr (!(D == 128 && MASK)) __builtin_amdgcn_iglp_opt(2);
-        float rs0 = 0.f, rs1 = 0.f;  // two chains for the fp32 row sum
+        constexpr bool kSumRounded = std::is_same_v<TI, F16>;
+        float rs0 = 0.f, rs1 = 0.f;  // two chains for the row sum
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -ref));
-                if (r & 1) rs1 += s[kb][r];
-                else rs0 += s[kb][r];
+                if constexpr (!kSumRounded) {
+                    if (r & 1) rs1 += s[kb][r];
+                    else rs0 += s[kb][r];
+                }
             }
-        l_run += rs0 + rs1;
 
         // ---- P^T as the B operand: 16-key group t of block kb is registers 8t..8t+7
         u32x4 pb[NKB][2];
@@ -315,6 +319,29 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     pb[kb][t][j] = pack2<TI>(s[kb][8 * t + 2 * j], s[kb][8 * t + 2 * j + 1]);
+        if constexpr (kSumRounded) {
+            // fp16 inputs: the row sum is taken from the rounded P the P*V
+            // product uses, two values per v_dot2_f32_f16 (half the adds).
+            // fp16 keeps 11 significant bits, so each term is within 2^-11
+            // of its float32 value and the sum within 2^-11 relative: an LSE
+            // error of at most 4.9e-4. (bf16's 2^-9 would allow 2e-3, so the
+            // bf16 path sums the float32 values.)
+            const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        // through a scalar: a bit cast of the vector element
+                        // expression itself reads the wrong word in this compiler
+                        const u32 w = pb[kb][t][j];
+                        const f16x2 pp = __builtin_bit_cast(f16x2, w);
+                        if (j & 1) rs1 = __builtin_amdgcn_fdot2(pp, one, rs1, false);
+                        else rs0 = __builtin_amdgcn_fdot2(pp, one, rs0, false);
+                    }
+        }
+        l_run += rs0 + rs1;
 
         // ---- O^T += V_j^T P^T. Register j of the B operand above is key
         // 16t + 8(j/4) + 4*hh + j%4 of the block; the A operand must hold
