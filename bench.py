@@ -9,8 +9,10 @@ bf16, causal, d=128, N=8192, B=2, H=32. Before the W warm-up steps the step
 runs back to back for --settle-ms (300 ms) so that the GPU has left its idle
 clock, which it takes a few hundred milliseconds of load to do (the first
 ten launches after idle average 1.5 ms, the sustained rate is 1.05 ms); the
-JSON line reports that phase as `settle` and the shader clock sampled during
-the K timed steps as `clock`.
+JSON line reports that phase as `settle`, and as `clock` the kernel's clock
+from the committed rocprofv3 counters of this kernel and shape
+(GRBM_GUI_ACTIVE cycles over kernel time) next to the SMU's own reading when
+its metrics table (refreshed about once a second) updated during the run.
 
 --bwd times the backward (one fa_bwd call per step: the D/LSE pass, the
 dK/dV kernel and the dQ kernel) on the forward's output, with nominal
@@ -152,21 +154,23 @@ def traffic(workload, kernel=KERNEL_PREFIX, tile=None):
 
 
 class ClockSampler:
-    """Samples the GPU's current shader clock (MHz) from the SMU through
-    amdsmi (else rocm-smi) in a background thread while `active`; reports
-    the median of the samples taken. The SMU figure is an average over its
-    own short window, so it is a reading of the clock, not a cycle count."""
+    """Reads the GPU's shader clock from the SMU metrics table through amdsmi
+    (current_gfxclk, MHz) in a background thread while `active`. The table
+    is refreshed about once a second, so only readings whose table timestamp
+    changed after the sampler started count; a shorter run gets none."""
 
-    def __init__(self, period_s=0.002):
+    def __init__(self, period_s=0.005):
         self.period_s = period_s
         self.samples = []
         self.active = False
         self.source = None
         self._stop = False
+        self._start_stamp = None
         self._read = self._open()
         self._thread = None
         if self._read is not None:
             import threading
+            self._start_stamp = self._read()[0]
             self._thread = threading.Thread(target=self._loop, daemon=True)
             self._thread.start()
 
@@ -175,18 +179,25 @@ class ClockSampler:
             import amdsmi
             amdsmi.amdsmi_init()
             handle = amdsmi.amdsmi_get_processor_handles()[0]
-            gfx = amdsmi.AmdSmiClkType.GFX
-            amdsmi.amdsmi_get_clock_info(handle, gfx)
-            self.source = "amdsmi_get_clock_info(GFX).clk"
-            return lambda: float(amdsmi.amdsmi_get_clock_info(handle, gfx)["clk"])
+
+            def read():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                return m["system_clock_counter"], float(m["current_gfxclk"])
+            read()
+            self.source = "amdsmi gpu_metrics current_gfxclk"
+            return read
         except Exception:
             return None
 
     def _loop(self):
+        last = self._start_stamp
         while not self._stop:
             if self.active:
                 try:
-                    self.samples.append(self._read())
+                    stamp, mhz = self._read()
+                    if stamp != last:
+                        self.samples.append(mhz)
+                        last = stamp
                 except Exception:
                     pass
             time.sleep(self.period_s)
@@ -199,8 +210,20 @@ class ClockSampler:
     def report(self):
         if not self.samples:
             return None
-        return {"median_mhz": _median(self.samples), "min_mhz": min(self.samples), "max_mhz": max(self.samples),
-                "samples": len(self.samples), "source": self.source}
+        return {"median_mhz": _median(self.samples), "samples": len(self.samples), "source": self.source}
+
+
+def clock_report(sampler, workload, kernel, tile):
+    """The clock the kernel runs at: GRBM_GUI_ACTIVE cycles over kernel time
+    from the committed rocprofv3 counter summary of this kernel, workload and
+    tile (when taken on the current sources), and the SMU's reading when its
+    metrics table refreshed during the run."""
+    from online_softmax_03_amd import profiling
+    c = profiling.current_counters(workload, kernel, tile)
+    return {"counter_ghz": None if c is None else round(c["clock_ghz"], 3),
+            "counter_mfma_busy": None if c is None else round(c["mfma_busy"], 4),
+            "counter_source": None if c is None else os.path.relpath(profiling.counters_file(workload, kernel), ROOT),
+            "smu": sampler.report()}
 
 
 def settle(step, settle_ms):
@@ -226,7 +249,7 @@ def settle(step, settle_ms):
 def timed_steps(step, stream, steps, warmup, clock=None):
     """Runs `warmup` untimed steps, then `steps` timed ones with a HIP event
     pair around each on `stream`. Returns (wall seconds, per-launch ms list).
-    `clock` (a ClockSampler) samples during the timed steps."""
+    `clock` (a ClockSampler) stops sampling when the timed steps end."""
     import torch
     for _ in range(warmup):
         step()
@@ -234,8 +257,6 @@ def timed_steps(step, stream, steps, warmup, clock=None):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
-    if clock is not None:
-        clock.active = True
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
@@ -319,8 +340,9 @@ def bench_softmax(args):
     def step():
         S.softmax_rows(xd, out_dtype=y.dtype, out=y, lse=lse)
 
-    settled = settle(step, args.settle_ms) if args.settle_ms > 0 else 0
     clock = ClockSampler()
+    clock.active = True
+    settled = settle(step, args.settle_ms) if args.settle_ms > 0 else 0
     wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup, clock)
     clock.close()
     avg_s = sum(launch_ms) / len(launch_ms) / 1e3
@@ -356,7 +378,7 @@ def bench_softmax(args):
                      "traffic": hbm_bytes, "traffic_detail": hbm_detail, "kernel": kernel,
                      "avg_launch_ms": round(avg_s * 1e3, 4),
                      "min_launch_ms": round(min(launch_ms), 4)},
-        "clock": clock.report(),
+        "clock": clock_report(clock, w.name, kernel, None),
         "settle": {"ms": args.settle_ms, "steps": settled},
     }
     if not args.no_cpu_baseline:
@@ -438,8 +460,9 @@ def main():
 
     # the GPU leaves its idle clock first; then per-launch HIP events on the
     # stream the kernel is launched on, with the shader clock sampled alongside
-    settled = settle(step, args.settle_ms) if args.settle_ms > 0 else 0
     clock = ClockSampler()
+    clock.active = True
+    settled = settle(step, args.settle_ms) if args.settle_ms > 0 else 0
     wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup, clock)
     clock.close()
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
@@ -499,7 +522,8 @@ def main():
                      "min_launch_ms": round(min(launch_ms), 4),
                      **({"flushed_mib": args.flush_mib, "flushed_median_launch_ms": round(_median(flushed), 4),
                          "flushed_min_launch_ms": round(min(flushed), 4)} if flushed else {})},
-        "clock": clock.report(),
+        "clock": clock_report(clock, w.name, kernel, None if fp8 else tile) if (splits is None and not args.bwd)
+        else {"smu": clock.report()},
         "settle": {"ms": args.settle_ms, "steps": settled},
     }
     if not args.no_cpu_baseline and not args.bwd:

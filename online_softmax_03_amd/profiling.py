@@ -194,6 +194,7 @@ def _report(a) -> None:
     if a.pmc:
         avg_ms = {r["Name"]: float(r["AverageNs"]) / 1e6 for r in stats}
         kc = _kernel_counters(a.pmc)
+        _counters_json(a, kc, avg_ms)
         lines += ["", "## Counters (rocprofv3 --pmc, one run)", "", "```"] + (a.pmc_command or []) + [
             "```", "",
             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); clock = "
@@ -209,10 +210,75 @@ def _report(a) -> None:
                          f"{xcd_cycles / (avg_ms[name] * 1e-3) / 1e9:.2f} | "
                          f"{c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:.2f} | "
                          f"{c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:.2f} | {c['SQ_LDS_BANK_CONFLICT']:.0f} |")
+    if a.l2:
+        l2 = _kernel_counters(a.l2)
+        lines += ["", "## L2 (rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum, one run)", "", "```"] + (a.l2_command or []) + [
+            "```", "", "| kernel | L2 hit | TCC_MISS x 128 B per launch (MiB) |", "|---|---|---|"]
+        for name in sorted(l2, key=lambda n: -l2[n].get("TCC_MISS_sum", 0.0)):
+            c = l2[name]
+            if "TCC_HIT_sum" not in c or a.kernel not in name:
+                continue
+            hit = c["TCC_HIT_sum"] / max(1.0, c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+            lines.append(f"| `{name[:80]}` | {100 * hit:.1f}% | {c['TCC_MISS_sum'] * L2_LINE / 2**20:.1f} |")
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
+
+def counters_file(workload: str, kernel: str = "attn_fwd_kernel") -> str:
+    return os.path.join(PROFILES, f"{kernel}_{workload}_counters.json")
+
+
+def _counters_json(a, kc, avg_ms) -> None:
+    """Writes the counter summary of the profiled kernel (the one with the
+    most MFMA instructions): effective clock, MFMA busy fraction, instruction
+    mix, and with --l2 the L2 hit rate; stamped with the source hash and tile
+    so bench.py quotes it only for the same kernel and shape."""
+    names = [n for n in kc if kc[n].get("SQ_INSTS_MFMA") and n in avg_ms]
+    if not names:
+        return
+    name = max(names, key=lambda n: kc[n]["SQ_INSTS_MFMA"])
+    c = kc[name]
+    xcd_cycles = c["GRBM_GUI_ACTIVE"] / N_XCD
+    out = {
+        "workload": a.workload, "kernel": a.kernel, "kernel_symbol": name,
+        "tile": [int(t) for t in a.tile.split(",")] if a.tile else None,
+        "source_hash": source_hash(_family(a.kernel)),
+        "avg_launch_ms": avg_ms[name],
+        "clock_ghz": xcd_cycles / (avg_ms[name] * 1e-3) / 1e9,
+        "mfma_busy": c["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * N_SIMD),
+        "valu_per_mfma": c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"],
+        "lds_per_mfma": c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"],
+        "lds_bank_conflicts": c["SQ_LDS_BANK_CONFLICT"],
+        "vgpr_count_rocprofv3": c.get("VGPR_Count"),
+        "commands": (a.command or []) + (a.pmc_command or []) + (a.l2_command or []),
+    }
+    if a.l2:
+        l2 = _kernel_counters(a.l2).get(name, {})
+        if "TCC_HIT_sum" in l2:
+            out["l2_hit"] = l2["TCC_HIT_sum"] / max(1.0, l2["TCC_HIT_sum"] + l2["TCC_MISS_sum"])
+            out["tcc_miss_bytes_per_launch"] = l2["TCC_MISS_sum"] * L2_LINE
+    with open(counters_file(a.workload, a.kernel), "w") as f:
+        json.dump(out, f, indent=2)
+
+
+def current_counters(workload: str, kernel: str = "attn_fwd_kernel", tile=None):
+    """The committed counter summary for `workload` if it was taken on the
+    current kernel sources and the same tile shape, else None."""
+    path = counters_file(workload, kernel)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash(_family(kernel)):
+        return None
+    if tile is not None and tuple(t.get("tile") or ()) != tuple(tile):
+        return None
+    return t
+
+
+# L2 (TCC) line size on MI355X, bytes
+L2_LINE = 128
 
 # MI355X: 8 XCDs (GRBM counters are summed over them), 256 CUs x 4 SIMDs.
 N_XCD = 8
@@ -256,9 +322,9 @@ def _tiles(a) -> None:
               "/ the unprofiled launch time. TFLOP/s and % of peak from the bench line of a separate, unprofiled "
               "run of the same configuration.", "",
               "| configuration | kernel | TFLOP/s | % of peak | MFMA busy | clock (GHz) | VALU / MFMA | LDS / MFMA "
-              "| LDS bank conflicts | HBM read + write (MiB) | HBM GB/s | VGPR (rocprofv3) | scratch |",
-              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
-    for label, bench_path, pmc, fetch_dir, write_dir in a.run:
+              "| LDS bank conflicts | HBM read + write (MiB) | HBM GB/s | L2 hit | VGPRs allocated | scratch |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for label, bench_path, pmc, fetch_dir, write_dir, l2_dir in a.run:
         with open(bench_path) as fh:
             bench = json.loads([l for l in fh if l.startswith("{")][-1])
         rf = bench["roofline"]
@@ -273,15 +339,22 @@ def _tiles(a) -> None:
         wk = _counter_rows(write_dir, "WRITE_SIZE", name)
         rd = sum(fk) / len(fk) * f_factor * 1024.0
         wr = sum(wk) / len(wk) * w_factor * 1024.0
+        l2 = _kernel_counters(l2_dir).get(name, {})
+        hit = (f"{100 * l2['TCC_HIT_sum'] / max(1.0, l2['TCC_HIT_sum'] + l2['TCC_MISS_sum']):.1f}%"
+               if "TCC_HIT_sum" in l2 else "n/a")
+        vg = int(float(c["VGPR_Count"])) * 2 if c.get("VGPR_Count") not in (None, "") else "n/a"
         lines.append(
             f"| {label} | `{name[:90]}` | {rf['achieved']:.1f} | {100 * rf['frac']:.1f}% | {100 * busy:.1f}% | "
             f"{clock:.2f} | {c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:.2f} | "
             f"{c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:.2f} | {c['SQ_LDS_BANK_CONFLICT']:.0f} | "
-            f"{rd / 2**20:.0f} + {wr / 2**20:.0f} | {(rd + wr) / t / 1e9:.0f} | "
-            f"{c['VGPR_Count']} (+{c['Accum_VGPR_Count']} acc) | {c['Scratch_Size']} |")
+            f"{rd / 2**20:.0f} + {wr / 2**20:.0f} | {(rd + wr) / t / 1e9:.0f} | {hit} | {vg} | "
+            f"{c['Scratch_Size']} |")
     lines += ["", "The clock column divides the counted cycles by the unprofiled launch time, so it is an estimate "
-              "of the clock the kernel ran at. rocprofv3's VGPR_Count column is reported as is; the compiler's "
-              "register counts follow."]
+              "of the clock the kernel ran at. VGPRs allocated = rocprofv3's VGPR_Count x 2: rocprofv3 "
+              "multiplies the kernel descriptor's register granules by 4, but gfx950's unified register file "
+              "allocates 8 registers per granule (e.g. the 128 x 32 tile: the compiler's 162 VGPRs round up to "
+              "21 granules = 168 registers, which rocprofv3 prints as 84). SQ_INSTS_VALU counts the MFMA "
+              "instructions too, so VALU / MFMA includes 1 for the MFMA itself."]
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -314,10 +387,13 @@ def main():
     r.add_argument("--command", nargs="*", default=[])
     r.add_argument("--pmc", default=None)
     r.add_argument("--pmc-command", nargs="*", default=[])
+    r.add_argument("--l2", default=None, help="rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum output directory")
+    r.add_argument("--l2-command", nargs="*", default=[])
+    r.add_argument("--tile", default=None, help="B_r,B_c of the profiled launch")
     r.add_argument("--out", required=True)
     t = sub.add_parser("tiles")
-    t.add_argument("--run", nargs=5, action="append",
-                   metavar=("LABEL", "BENCH_JSON", "PMC_DIR", "FETCH_DIR", "WRITE_DIR"), required=True)
+    t.add_argument("--run", nargs=6, action="append",
+                   metavar=("LABEL", "BENCH_JSON", "PMC_DIR", "FETCH_DIR", "WRITE_DIR", "L2_DIR"), required=True)
     t.add_argument("--copy-fetch", required=True)
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-mib", type=int, default=1024)

@@ -48,7 +48,8 @@ def test_one_json_line_with_roofline_and_cpu_baseline():
     assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0 and cb["cores"] >= 1
     assert "rows of bf16_causal_n8192_d128" in cb["sample"]
     assert d["settle"]["steps"] >= 1
-    assert d["clock"] is None or 100 <= d["clock"]["median_mhz"] <= 2500
+    assert d["clock"]["counter_ghz"] is None or 0.5 <= d["clock"]["counter_ghz"] <= 2.5
+    assert d["clock"]["smu"] is None or 100 <= d["clock"]["smu"]["median_mhz"] <= 2500
 
 
 @pytest.mark.gpu
