@@ -482,7 +482,7 @@ def main():
         effective = {"flops_per_step": eff_flops, "tflops": round(eff_flops / avg_launch_s / 1e12, 2),
                      "fraction_of_nominal": round(eff_flops / flops, 4)}
     peak = PEAK_TFLOPS[w.in_dtype]
-    kernel = "attn_fwd_fp8_kernel" if fp8 else KERNEL_PREFIX
+    kernel = "attn_fwd_fp8_kernel" if fp8 else ("attn_fwd_f32_kernel" if w.in_dtype == "f32" else KERNEL_PREFIX)
     hbm_bytes, hbm_detail = (traffic(w.name, kernel, None if fp8 else tile) if (splits is None and not args.bwd)
                              else (None, None))
     # the roofline credits only the allowed (query, key) pairs: padded keys
