@@ -128,6 +128,12 @@ __device__ __forceinline__ void wait_vmcnt0() {
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    // s_waitcnt lgkmcnt(0); vmcnt (both fields) and expcnt left at their
+    // no-wait maxima.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
 template <typename T>
 __device__ __forceinline__ void store_row4(char* dst, const float* v4, float inv);
 

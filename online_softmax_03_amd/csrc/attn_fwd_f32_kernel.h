@@ -193,14 +193,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(Params p) {
             m_run = m_new;
         }
         const float ref = (m_run == -INFINITY) ? 0.f : m_run * c;
+        // two chains for the row sum, each started from its first term
         float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -ref));
-                if (r & 1) rs1 += s[kb][r];
-                else rs0 += s[kb][r];
+                float& rs = (r & 1) ? rs1 : rs0;
+                rs = (kb == 0 && r < 2) ? s[kb][r] : rs + s[kb][r];
             }
         l_run += rs0 + rs1;
 

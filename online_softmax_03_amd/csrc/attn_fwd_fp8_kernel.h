@@ -282,14 +282,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
             k = 0;
         }
         const float ref = ((frame == -INFINITY) ? 0.f : frame + (float)k) - (float)MAXOFF;
+        // two chains for the row sum, each started from its first term
         float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -ref));
-                if (r & 1) rs1 += s[kb][r];
-                else rs0 += s[kb][r];
+                float& rs = (r & 1) ? rs1 : rs0;
+                rs = (kb == 0 && r < 2) ? s[kb][r] : rs + s[kb][r];
             }
         l_run += __builtin_ldexpf(rs0 + rs1, k);
         const int pscale = 127 + k;  // E8M0 2^k

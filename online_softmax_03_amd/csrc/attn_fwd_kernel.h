@@ -37,7 +37,7 @@
 //      ds_read_b64_tr_b16 in that same key order. No LDS round trip for P.
 //      The row sum l is accumulated from the fp32 P before rounding (as the
 //      deferred row sum of "Online Softmax 算法详解" section 4.6 is) for bf16
-//      inputs: summing the rounded values instead would put bf16's 2^-9
+//      inputs: summing the rounded values instead would put bf16's 2^-8
 //      relative error straight into the LSE. For fp16 inputs it is taken from
 //      the rounded P (2^-11 relative, an LSE error of at most 4.9e-4), two
 //      values per v_dot2_f32_f16.
@@ -298,15 +298,18 @@ void attn_fwd_kernel(Params p) {
         // tiles' masked forms grow by 40-50 of them) and gains nothing.
         if constexpr (!(D == 128 && MASK)) __builtin_amdgcn_iglp_opt(2);
         constexpr bool kSumRounded = std::is_same_v<TI, F16>;
-        float rs0 = 0.f, rs1 = 0.f;  // two chains for the row sum
+        // Two chains for the row sum. The float32 sums start from their
+        // first terms rather than from 0 (the same value: exp2 is never -0),
+        // which saves an add per chain and tile.
+        float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -ref));
                 if constexpr (!kSumRounded) {
-                    if (r & 1) rs1 += s[kb][r];
-                    else rs0 += s[kb][r];
+                    float& rs = (r & 1) ? rs1 : rs0;
+                    rs = (kb == 0 && r < 2) ? s[kb][r] : rs + s[kb][r];
                 }
             }
 
@@ -324,8 +327,9 @@ void attn_fwd_kernel(Params p) {
             // product uses, two values per v_dot2_f32_f16 (half the adds).
             // fp16 keeps 11 significant bits, so each term is within 2^-11
             // of its float32 value and the sum within 2^-11 relative: an LSE
-            // error of at most 4.9e-4. (bf16's 2^-9 would allow 2e-3, so the
-            // bf16 path sums the float32 values.)
+            // error of at most 4.9e-4. (bf16 keeps 8 significant bits, whose
+            // 2^-8 would allow 3.9e-3, so the bf16 path sums the float32
+            // values.)
             const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)

@@ -26,10 +26,10 @@ namespace fa {
         FA_SM_RES(TI, IN, TO, OUT, 16, 1, 4), FA_SM_RES(TI, IN, TO, OUT, 16, 1, 8)
 #define FA_SM_STREAMS(TI, IN, TO, OUT) FA_SM_STREAM(TI, IN, TO, OUT, 1), FA_SM_STREAM(TI, IN, TO, OUT, 0)
 #define FA_SM_PAIR(TI, IN, TO, OUT)                                                                    \
-    FA_SM_RES_ALL(TI, IN, TO, OUT), FA_SM_RES_LDS(TI, IN, TO, OUT, 8, 8), FA_SM_RES_LDS(TI, IN, TO, OUT, 12, 8), \
+    FA_SM_RES_ALL(TI, IN, TO, OUT), FA_SM_RES_LDS(TI, IN, TO, OUT, 8, 8), FA_SM_RES_LDS(TI, IN, TO, OUT, 11, 9), \
         FA_SM_STREAMS(TI, IN, TO, OUT)
 #define FA_SM_PAIR_F32(TI, IN, TO, OUT)                                                                  \
-    FA_SM_RES_ALL(TI, IN, TO, OUT), FA_SM_RES_LDS(TI, IN, TO, OUT, 16, 8), FA_SM_RES_LDS(TI, IN, TO, OUT, 24, 8), \
+    FA_SM_RES_ALL(TI, IN, TO, OUT), FA_SM_RES_LDS(TI, IN, TO, OUT, 16, 8), FA_SM_RES_LDS(TI, IN, TO, OUT, 23, 9), \
         FA_SM_STREAMS(TI, IN, TO, OUT)
 
 static const SoftmaxEntry kSmEntries[] = {

@@ -50,7 +50,10 @@ int fa_softmax_fwd(const void* x, void* y, float* lse, long long rows, int cols,
     }
     if (!pick) return FA_ERR_DTYPE;
     const long long rpb = pick->kind == fa::kSmResident ? pick->rpb : 1;  // one row per workgroup otherwise
-    const long long grid = (rows + rpb - 1) / rpb;
+    long long grid = (rows + rpb - 1) / rpb;
+    // the register + LDS form walks rows with one workgroup per compute unit
+    // of the 256
+    if (pick->kind == fa::kSmResidentLds && grid > 256) grid = 256;
     fa::SoftmaxParams sp;
     sp.x = x;
     sp.y = y;

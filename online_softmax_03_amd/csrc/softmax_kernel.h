@@ -26,7 +26,8 @@
 //   softmax_resident_lds_kernel: rows longer than the registers of one
 //     workgroup hold: each thread keeps part of its slice in registers and
 //     the rest in LDS (loaded there by LDS DMA, no registers in between), so
-//     x is still read from HBM once.
+//     x is still read from HBM once. One workgroup per compute unit walks
+//     several rows and loads the next row while it writes the current one.
 //   softmax_stream_kernel: rows too long for registers and LDS, or whose
 //     length is not a whole number of 16-byte vectors. Pass 1 streams the row and keeps
 //     a running (m, l) per thread, updated per vector; pass 2 streams it again
@@ -271,14 +272,23 @@ __global__ __launch_bounds__(WPR * RPB * 64) void softmax_resident_kernel(Softma
 
 // ---------------------------------------------------------------- resident rows, registers + LDS
 
-// One workgroup of 1024 threads per row. Thread t holds vectors j = i*1024 + t
-// for i < VPT in registers and for VPT <= i < VPT + VLDS in LDS, at byte
-// ((i - VPT)*1024 + t)*16 of the workgroup's buffer: a wave's LDS DMA writes
-// 64 consecutive 16-byte slots, so each thread reads back only what its own
-// wave loaded (no barrier needed for that), and consecutive lanes read
-// consecutive 16-byte slots (no bank conflicts). The LDS part is read twice
-// (maximum and sum, then output) and its exponentials are recomputed on the
-// second read instead of being stored.
+// Workgroups of 1024 threads, one row at a time. Thread t holds vectors
+// j = i*1024 + t of its row for i < VPT in registers and for
+// VPT <= i < VPT + VLDS in LDS, at byte ((i - VPT)*1024 + t)*16 of the
+// workgroup's buffer: a wave's LDS DMA writes 64 consecutive 16-byte slots,
+// so each thread reads back only what its own wave loaded (no barrier needed
+// for that), and consecutive lanes read consecutive 16-byte slots (no bank
+// conflicts). The LDS part is read twice (maximum and sum, then output) and
+// its exponentials are recomputed on the second read instead of being
+// stored.
+//
+// The LDS part leaves room for one such workgroup per compute unit, so the
+// grid is at most one per compute unit and each workgroup walks the rows
+// blockIdx.x, blockIdx.x + gridDim.x, ... As soon as a thread has written
+// out one of its vectors of row r, it starts loading the same vector of its
+// next row into the register or LDS slot just freed: the stores of one row
+// and the loads of the next are in flight together, instead of each
+// workgroup's memory traffic stopping between rows.
 template <typename TI, typename TO, int VPT, int VLDS>
 __global__ __launch_bounds__(1024) void softmax_resident_lds_kernel(SoftmaxParams sp) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -286,43 +296,49 @@ __global__ __launch_bounds__(1024) void softmax_resident_lds_kernel(SoftmaxParam
     constexpr int E = VecIn<TI>::kN;
     constexpr int NW = NT / 64;
     __shared__ __attribute__((aligned(1024))) char s_x[VLDS * NT * 16];
-    __shared__ float s_m[NW], s_l[NW];
+    // per-wave states by row parity: a wave that runs ahead writes the other
+    // half while slower waves still read this row's
+    __shared__ float s_m[2][NW], s_l[2][NW];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const long long row = blockIdx.x;
     const int nvec = sp.cols / E;
-    const char* xr = reinterpret_cast<const char*>(sp.x) + row * (long long)sp.cols * TI::kBytes;
-    char* yr = reinterpret_cast<char*>(sp.y) + row * (long long)sp.cols * TO::kBytes;
+    const long long xrow_bytes = (long long)sp.cols * TI::kBytes;
+    const long long yrow_bytes = (long long)sp.cols * TO::kBytes;
 
-    // Buffer resources over the row, addressed by per-lane byte offsets only
+    // Buffer resources over one row, addressed by per-lane byte offsets only
     // (the hardware's range check covers the per-lane offset, not a scalar
     // one): vector j of x at j * 16. Vectors past the end of the row fall
     // outside the resource (read as zero, stores dropped) and are excluded
     // from the maximum and the sum by j < nvec.
-    const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc((void*)xr, 0, nvec * 16, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t ry =
-        __builtin_amdgcn_make_buffer_rsrc((void*)yr, 0, nvec * E * TO::kBytes, kBufferFlags);
-    const u32 xoff = (u32)t * 16u;
-    const u32 yoff = (u32)t * (E * TO::kBytes);
-    // LDS part first, so its loads are in flight while the register part loads.
-#pragma unroll
-    for (int k = 0; k < VLDS; ++k)
+    auto x_rsrc = [&](long long row) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(reinterpret_cast<const char*>(sp.x) + row * xrow_bytes), 0, nvec * 16, kBufferFlags);
+    };
+    auto y_rsrc = [&](long long row) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<char*>(sp.y) + row * yrow_bytes), 0,
+                                                 nvec * E * TO::kBytes, kBufferFlags);
+    };
+    // Per-lane byte offsets of vector i: xoff + i*NT*16 (x), yoff + ... (y).
+    // The per-row loop below makes xoff and yoff opaque at the start of each
+    // row, so those sums are formed where they are used instead of being
+    // hoisted out of the loop and held in registers throughout.
+    u32 xoff = (u32)t * 16u;
+    u32 yoff = (u32)t * (E * TO::kBytes);
+    auto load_lds = [&](__amdgpu_buffer_rsrc_t rx, int k) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (FA_LDS void*)(s_x + (k * NT + wave * 64) * 16), 16,
                                                  xoff + (u32)((VPT + k) * NT) * 16u, 0, 0, 0);
-    float v[VPT][E];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
+    };
+    // A register vector arrives as its raw 16 bytes in the first four words
+    // of its float slots and is widened in place before use (the slots are
+    // its own: the next row's vector i takes the registers of this row's
+    // vector i as soon as that one is written out).
+    auto load_reg = [&](__amdgpu_buffer_rsrc_t rx, int i, float* vi) {
         const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + (u32)(i * NT) * 16u, 0, 0);
-        VecIn<TI>::cvt(u, v[i]);
-        if (!(i * NT + t < nvec)) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) v[i][e] = -INFINITY;
-        }
-    }
-    wait_vmcnt0();
+        for (int w = 0; w < 4; ++w) vi[w] = __uint_as_float(u[w]);
+    };
     auto lds_vec = [&](int k, float* w) {
         const int j = (VPT + k) * NT + t;
         if (j < nvec) {
@@ -333,71 +349,110 @@ __global__ __launch_bounds__(1024) void softmax_resident_lds_kernel(SoftmaxParam
         }
     };
 
-    // the slice's maximum over both parts, then its exponentials and their sum
-    float m = -INFINITY;
+    long long row = blockIdx.x;
+    float v[VPT][E];
+    {
+        const __amdgpu_buffer_rsrc_t rx = x_rsrc(row);
+        // LDS part first, so its loads are in flight while the register part loads
 #pragma unroll
-    for (int i = 0; i < VPT; ++i)
+        for (int k = 0; k < VLDS; ++k) load_lds(rx, k);
 #pragma unroll
-        for (int e = 0; e < E; ++e) m = fmaxf(m, v[i][e]);
-    // (the LDS loops stay rolled: one vector in flight keeps the register
-    // part's budget)
-#pragma clang loop unroll(disable)
-    for (int k = 0; k < VLDS; ++k) {
-        float w[E];
-        lds_vec(k, w);
-#pragma unroll
-        for (int e = 0; e < E; ++e) m = fmaxf(m, w[e]);
+        for (int i = 0; i < VPT; ++i) load_reg(rx, i, v[i]);
     }
-    const float mref = (m == -INFINITY) ? 0.f : m;
-    float l0 = 0.f, l1 = 0.f;
+    for (int par = 0;; par ^= 1) {
+        asm volatile("" : "+v"(xoff), "+v"(yoff));
+        const long long next = row + gridDim.x;
+        const bool has_next = next < sp.rows;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i)
+        for (int i = 0; i < VPT; ++i) {
+            const u32x4 u = {__float_as_uint(v[i][0]), __float_as_uint(v[i][1]), __float_as_uint(v[i][2]),
+                             __float_as_uint(v[i][3])};
+            VecIn<TI>::cvt(u, v[i]);
+            if (!(i * NT + t < nvec)) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            v[i][e] = __builtin_amdgcn_exp2f((v[i][e] - mref) * kSmLog2e);
-            if (e & 1) l1 += v[i][e];
-            else l0 += v[i][e];
+                for (int e = 0; e < E; ++e) v[i][e] = -INFINITY;
+            }
+        }
+        wait_vmcnt0();  // this wave's LDS DMA of the row has landed too
+
+        // the slice's maximum over both parts, then its exponentials and their sum
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int e = 0; e < E; ++e) m = fmaxf(m, v[i][e]);
+        // (the LDS loops stay rolled: one vector in flight keeps the register
+        // part's budget)
+#pragma clang loop unroll(disable)
+        for (int k = 0; k < VLDS; ++k) {
+            float w[E];
+            lds_vec(k, w);
+#pragma unroll
+            for (int e = 0; e < E; ++e) m = fmaxf(m, w[e]);
+        }
+        const float mref = (m == -INFINITY) ? 0.f : m;
+        float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                v[i][e] = __builtin_amdgcn_exp2f((v[i][e] - mref) * kSmLog2e);
+                if (e & 1) l1 += v[i][e];
+                else l0 += v[i][e];
+            }
+#pragma clang loop unroll(disable)
+        for (int k = 0; k < VLDS; ++k) {
+            float w[E];
+            lds_vec(k, w);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float x = __builtin_amdgcn_exp2f((w[e] - mref) * kSmLog2e);
+                if (e & 1) l1 += x;
+                else l0 += x;
+            }
+        }
+        const float m_slice = m;
+        float l = l0 + l1;
+
+        // the row's state: lanes, then the waves in a fixed order
+        sm_wave_merge(m, l);
+        if (lane == 0) {
+            s_m[par][wave] = m;
+            s_l[par][wave] = l;
+        }
+        __syncthreads();
+        m = s_m[par][0];
+        l = s_l[par][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) sm_merge(m, l, s_m[par][w], s_l[par][w]);
+
+        // output, y = e^(x - m_slice) * e^(m_slice - m) / l, each vector's
+        // slot refilled with the next row's vector once it is written
+        const bool dead = !(l > 0.f);
+        const float sc = dead ? 0.f : sm_rescale(m_slice, m) / l;
+        const __amdgpu_buffer_rsrc_t ry = y_rsrc(row);
+        const __amdgpu_buffer_rsrc_t rn = x_rsrc(has_next ? next : row);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            store_scaled_buf<TO, E>(ry, yoff + (u32)(i * NT) * (E * TO::kBytes), v[i], sc);
+            if (has_next) load_reg(rn, i, v[i]);
         }
 #pragma clang loop unroll(disable)
-    for (int k = 0; k < VLDS; ++k) {
-        float w[E];
-        lds_vec(k, w);
+        for (int k = 0; k < VLDS; ++k) {
+            float w[E];
+            lds_vec(k, w);
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float x = __builtin_amdgcn_exp2f((w[e] - mref) * kSmLog2e);
-            if (e & 1) l1 += x;
-            else l0 += x;
+            for (int e = 0; e < E; ++e) w[e] = __builtin_amdgcn_exp2f((w[e] - mref) * kSmLog2e);
+            store_scaled_buf<TO, E>(ry, yoff + (u32)((VPT + k) * NT) * (E * TO::kBytes), w, sc);
+            if (has_next) {
+                wait_lgkmcnt0();  // the wave's read of slot k is done before the DMA refills it
+                load_lds(rn, k);
+            }
         }
+        if (t == 0 && sp.lse) sp.lse[row] = dead ? -INFINITY : m + __builtin_amdgcn_logf(l) * kLn2;
+        if (!has_next) break;
+        row = next;
     }
-    const float m_slice = m;
-    float l = l0 + l1;
-
-    // the row's state: lanes, then the waves in a fixed order
-    sm_wave_merge(m, l);
-    if (lane == 0) {
-        s_m[wave] = m;
-        s_l[wave] = l;
-    }
-    __syncthreads();
-    m = s_m[0];
-    l = s_l[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) sm_merge(m, l, s_m[w], s_l[w]);
-
-    // output: y = e^(x - m_slice) * e^(m_slice - m) / l
-    const bool dead = !(l > 0.f);
-    const float sc = dead ? 0.f : sm_rescale(m_slice, m) / l;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) store_scaled_buf<TO, E>(ry, yoff + (u32)(i * NT) * (E * TO::kBytes), v[i], sc);
-#pragma clang loop unroll(disable)
-    for (int k = 0; k < VLDS; ++k) {
-        float w[E];
-        lds_vec(k, w);
-#pragma unroll
-        for (int e = 0; e < E; ++e) w[e] = __builtin_amdgcn_exp2f((w[e] - mref) * kSmLog2e);
-        store_scaled_buf<TO, E>(ry, yoff + (u32)((VPT + k) * NT) * (E * TO::kBytes), w, sc);
-    }
-    if (t == 0 && sp.lse) sp.lse[row] = dead ? -INFINITY : m + __builtin_amdgcn_logf(l) * kLn2;
 #endif
 }
 

@@ -10,7 +10,7 @@ rows. y and LSE are pre-filled with NaN so that an unwritten element fails.
 
 Tolerances, from the arithmetic: the kernel works in float32 and rounds y
 once to the output dtype, so |dy| <= rel * y + abs with rel = 4e-3 for bf16
-output (half an ulp is 2^-9 of the value), 1e-3 for fp16 (2^-11, plus the
+output (half an ulp is at most 2^-8 of the value), 1e-3 for fp16 (2^-11, plus the
 float32 terms), 2e-5 for fp32 (exp2 of an argument carrying up to ~100 * 2^-24
 absolute error, and the sum's rounding); abs covers fp16 subnormals. LSE is
 a float32 output, ln of a normaliser summed over up to 2^17 terms plus the
@@ -112,6 +112,31 @@ def test_in_place(pair, cols):
     x = W.generate_softmax(w)
     y, lse = run_gpu(x, pair[1], inplace=True)
     compare(y, lse, x, pair[1], f"in place {pair} cols={cols}")
+
+
+# The register + LDS forms run one workgroup per compute unit (256) that walks
+# rows r, r + 256, ...: 517 rows give each workgroup two or three rows, and
+# the rows with no finite entry or a single one sit in the second and third
+# passes of their workgroups.
+ROW_WALK = [(("bf16", "bf16"), 131072, False), (("f16", "f32"), 163840, False), (("f32", "f32"), 98304, False),
+            (("f32", "f32"), 131072, True), (("bf16", "bf16"), 163840, True)]
+
+
+@pytest.mark.parametrize("pair,cols,inplace", ROW_WALK,
+                         ids=[f"{p[0]}->{p[1]}-{c}{'-inplace' if ip else ''}" for p, c, ip in ROW_WALK])
+def test_register_lds_row_walk(pair, cols, inplace):
+    rows = 517
+    w = BASE.with_shape(rows=rows, cols=cols, in_dtype=pair[0], out_dtype=pair[1], masked_frac=0.1,
+                        seed=3400 + cols)
+    x = W.generate_softmax(w)
+    x[300] = float("-inf")               # second pass of workgroup 44
+    x[513] = float("-inf")               # third pass of workgroup 1
+    x[513, 17] = -2.0
+    x[516] = float("-inf")               # third pass of the last workgroup with three rows
+    log(f"case softmax row walk {pair[0]}->{pair[1]} rows={rows} cols={cols} inplace={inplace}")
+    y, lse = run_gpu(x, pair[1], inplace=inplace)
+    e = compare(y, lse, x, pair[1], f"row walk {pair} cols={cols} inplace={inplace}")
+    log(f"  max|dy|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
 
 
 def test_without_lse():
