@@ -174,22 +174,44 @@ __device__ __forceinline__ float sm_rescale(float m, float ref) {
 
 // Merge of two partial states (m1, l1) and (m2, l2), in place into (m, l).
 // Symmetric in its two arguments, so every lane of a butterfly ends with the
-// same bits.
+// same bits: the two products are rounded separately (no contraction into a
+// fused multiply-add, which would round them differently depending on the
+// argument order) before the commutative add.
 __device__ __forceinline__ void sm_merge(float& m, float& l, float m2, float l2) {
+#pragma clang fp contract(off)
     const float mm = fmaxf(m, m2);
     const float ref = (mm == -INFINITY) ? 0.f : mm;
     l = l * sm_rescale(m, ref) + l2 * sm_rescale(m2, ref);
     m = mm;
 }
 
-// Merge over the 64 lanes of a wave; every lane ends with the wave's state.
-__device__ __forceinline__ void sm_wave_merge(float& m, float& l) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float m2 = __shfl_xor(m, off, 64);
-        const float l2 = __shfl_xor(l, off, 64);
-        sm_merge(m, l, m2, l2);
+// The value of lane l ^ K (K < 32) by ds_swizzle in its bit-mask mode (and
+// mask 0x1f, xor mask K, within each 32-lane half): no lane index needed.
+template <int K>
+__device__ __forceinline__ float lane_xor(float x) {
+    static_assert(K >= 1 && K <= 16, "xor within 32 lanes");
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (K << 10) | 0x1f));
+}
+
+template <int K>
+__device__ __forceinline__ void sm_xor_merge(float& m, float& l) {
+    if constexpr (K >= 1) {
+        sm_merge(m, l, lane_xor<K>(m), lane_xor<K>(l));
+        sm_xor_merge<K / 2>(m, l);
     }
+}
+
+// Merge over the 64 lanes of a wave; every lane ends with the wave's state.
+// The two 32-lane halves first, by v_permlane32_swap, which hands every lane
+// the states of lanes l % 32 and 32 + l % 32 in that order; then xor steps
+// of 16 ... 1 within each half.
+__device__ __forceinline__ void sm_wave_merge(float& m, float& l) {
+    const auto ms = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    const auto ls = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+    m = __uint_as_float(ms[0]);
+    l = __uint_as_float(ls[0]);
+    sm_merge(m, l, __uint_as_float(ms[1]), __uint_as_float(ls[1]));
+    sm_xor_merge<16>(m, l);
 }
 
 // ---------------------------------------------------------------- resident rows
@@ -272,9 +294,10 @@ __global__ __launch_bounds__(WPR * RPB * 64) void softmax_resident_kernel(Softma
 
 // ---------------------------------------------------------------- resident rows, registers + LDS
 
-// Workgroups of 1024 threads, one row at a time. Thread t holds vectors
-// j = i*1024 + t of its row for i < VPT in registers and for
-// VPT <= i < VPT + VLDS in LDS, at byte ((i - VPT)*1024 + t)*16 of the
+// Workgroups of NT threads (1024, or 768 where 168 registers per thread
+// hold more of the row than 128 do), one row at a time. Thread t holds
+// vectors j = i*NT + t of its row for i < VPT in registers and for
+// VPT <= i < VPT + VLDS in LDS, at byte ((i - VPT)*NT + t)*16 of the
 // workgroup's buffer: a wave's LDS DMA writes 64 consecutive 16-byte slots,
 // so each thread reads back only what its own wave loaded (no barrier needed
 // for that), and consecutive lanes read consecutive 16-byte slots (no bank
@@ -289,10 +312,10 @@ __global__ __launch_bounds__(WPR * RPB * 64) void softmax_resident_kernel(Softma
 // next row into the register or LDS slot just freed: the stores of one row
 // and the loads of the next are in flight together, instead of each
 // workgroup's memory traffic stopping between rows.
-template <typename TI, typename TO, int VPT, int VLDS>
-__global__ __launch_bounds__(1024) void softmax_resident_lds_kernel(SoftmaxParams sp) {
+template <typename TI, typename TO, int NT, int VPT, int VLDS>
+__global__ __launch_bounds__(NT) void softmax_resident_lds_kernel(SoftmaxParams sp) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int NT = 1024;
+    static_assert(NT % 256 == 0, "whole waves on every SIMD");
     constexpr int E = VecIn<TI>::kN;
     constexpr int NW = NT / 64;
     __shared__ __attribute__((aligned(1024))) char s_x[VLDS * NT * 16];
@@ -320,12 +343,15 @@ __global__ __launch_bounds__(1024) void softmax_resident_lds_kernel(SoftmaxParam
         return __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<char*>(sp.y) + row * yrow_bytes), 0,
                                                  nvec * E * TO::kBytes, kBufferFlags);
     };
-    // Per-lane byte offsets of vector i: xoff + i*NT*16 (x), yoff + ... (y).
-    // The per-row loop below makes xoff and yoff opaque at the start of each
-    // row, so those sums are formed where they are used instead of being
-    // hoisted out of the loop and held in registers throughout.
+    // Per-lane byte offsets of vector i: xoff + i*NT*16 (x) and
+    // yoff + i*NT*E*size (y), where yoff = xoff * E*size/16 (the same register
+    // when input and output elements have the same size). The per-row loop
+    // below makes xoff opaque at the start of each row, so those sums are
+    // formed where they are used instead of being hoisted out of the loop and
+    // held in registers throughout.
+    constexpr u32 kYScale = (u32)(E * TO::kBytes) / 16u;
+    static_assert(kYScale * 16u == (u32)(E * TO::kBytes), "whole output vectors");
     u32 xoff = (u32)t * 16u;
-    u32 yoff = (u32)t * (E * TO::kBytes);
     auto load_lds = [&](__amdgpu_buffer_rsrc_t rx, int k) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (FA_LDS void*)(s_x + (k * NT + wave * 64) * 16), 16,
                                                  xoff + (u32)((VPT + k) * NT) * 16u, 0, 0, 0);
@@ -360,7 +386,8 @@ __global__ __launch_bounds__(1024) void softmax_resident_lds_kernel(SoftmaxParam
         for (int i = 0; i < VPT; ++i) load_reg(rx, i, v[i]);
     }
     for (int par = 0;; par ^= 1) {
-        asm volatile("" : "+v"(xoff), "+v"(yoff));
+        asm volatile("" : "+v"(xoff));
+        const u32 yoff = xoff * kYScale;
         const long long next = row + gridDim.x;
         const bool has_next = next < sp.rows;
 #pragma unroll

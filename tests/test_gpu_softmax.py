@@ -68,10 +68,11 @@ def compare(y, lse, x, out_dtype, what):
 
 
 # register-resident capacities (16-bit elements): 512 ... 65536; register +
-# LDS shapes: 131072 and 163840 (16-bit), 98304 and 131072 (fp32); each
+# LDS shapes: 131072 and 165888 (16-bit), 98304 and 132096 (fp32); each
 # also one vector over, which moves to the next shape or the streamed form
 COLS = [1, 3, 4, 8, 24, 64, 100, 512, 520, 1024, 1032, 2048, 2056, 4096, 4104, 8192, 8200, 16384, 16392,
-        32768, 32776, 65536, 65544, 70001, 98304, 98308, 100000, 131072, 131076, 131080, 163840, 163848]
+        32768, 32776, 65536, 65544, 70001, 98304, 98308, 100000, 131072, 131076, 131080, 132096, 132100,
+        163840, 165888, 165896]
 
 
 @pytest.mark.parametrize("cols", COLS)
@@ -118,8 +119,8 @@ def test_in_place(pair, cols):
 # rows r, r + 256, ...: 517 rows give each workgroup two or three rows, and
 # the rows with no finite entry or a single one sit in the second and third
 # passes of their workgroups.
-ROW_WALK = [(("bf16", "bf16"), 131072, False), (("f16", "f32"), 163840, False), (("f32", "f32"), 98304, False),
-            (("f32", "f32"), 131072, True), (("bf16", "bf16"), 163840, True)]
+ROW_WALK = [(("bf16", "bf16"), 131072, False), (("f16", "f32"), 165888, False), (("f32", "f32"), 98304, False),
+            (("f32", "f32"), 132096, True), (("bf16", "bf16"), 163840, True)]
 
 
 @pytest.mark.parametrize("pair,cols,inplace", ROW_WALK,
