@@ -426,9 +426,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     bool kvalid = key < N;
     if constexpr (MASK) kvalid = kvalid && p.mask[(size_t)b * N + min(key, N - 1)] != 0;
     const bool all_valid = __builtin_amdgcn_ballot_w64(kvalid) == ~0ull;
+    // Padded keys get dK = dV = 0 and contribute nothing: a wave whose 32
+    // keys are all padded skips its products (it still takes part in the
+    // tile barriers), and a workgroup with no valid key skips its loads and
+    // the query loop and only stores its zeros.
+    const bool wave_has_key = __builtin_amdgcn_ballot_w64(kvalid) != 0;
+    const bool wg_has_key = !MASK || __syncthreads_or(wave_has_key ? 1 : 0) != 0;
 
     const int q_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
-    const int n_tiles = (N - q_begin + BQ - 1) / BQ;
+    const int n_tiles = wg_has_key ? (N - q_begin + BQ - 1) / BQ : 0;
 
     {
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -446,7 +452,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // The wave's 32 K rows into its own part of kbuf (row-major, chunks
     // swizzled as in the tiles); keys past N read as zero. Only this wave
     // reads them, so its own wait for the loads (the first tile's) suffices.
-    {
+    if (n_tiles > 0) {
         constexpr int KLOADS = 32 * ROWB / 1024;  // wave loads per wave
         const int kbytes = max(N - kw0, 0) * ROWB;
         const __amdgpu_buffer_rsrc_t rk =
@@ -528,7 +534,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
 
     auto compute_tile = [&](int tile, const char* buf) {
-        if (!wave_live) return;
+        if (!wave_live || !wave_has_key) return;
         const int q0 = q_begin + tile * BQ;
         const FA_LDS char* qt = (const FA_LDS char*)buf;
         const FA_LDS char* dt = (const FA_LDS char*)buf + TILEB;
@@ -611,7 +617,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
     };
 
-    issue_tile(0, buf0);
+    if (n_tiles > 0) issue_tile(0, buf0);
     for (int it = 0; it < n_tiles; it += 2) {
         wait_vmcnt0();
         __syncthreads();
