@@ -282,6 +282,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
             k = 0;
         }
         const float ref = ((frame == -INFINITY) ? 0.f : frame + (float)k) - (float)MAXOFF;
+        // the compiler's exponential/MFMA interleave schedule for the block
+        // below, as in the 16-bit kernel (0.5-0.7% here, the same results)
+        __builtin_amdgcn_iglp_opt(2);
         // two chains for the row sum, each started from its first term
         float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
