@@ -139,3 +139,44 @@ def test_full_size_headline_heads():
         got = [t[b:b + 1, h:h + 1].float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
         e = check(got, ref, "bf16", f"{C3} head ({b},{h})")
         log(f"  head ({b},{h}): rel errors dq={e[0]:.2e} dk={e[1]:.2e} dv={e[2]:.2e}")
+
+
+def _draw(i):
+    r = np.random.default_rng(50000 + i)
+    d = int(r.choice([64, 128]))
+    dtype = ["bf16", "f16"][int(r.integers(2))]
+    return dict(d=d, dtype=dtype, grad=["same", "f32"][int(r.integers(2))], causal=bool(r.integers(2)),
+                B=int(r.integers(1, 4)), H=int(r.integers(1, 5)), N=max(1, int(np.exp(r.uniform(0.0, np.log(500.0))))),
+                qk=float(r.choice([0.5, 1.0, 2.0])), mask=["none", "padding", "general"][int(r.integers(3))],
+                seed=51000 + i)
+
+
+RANDOM = [_draw(i) for i in range(40)]
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM)))
+def test_random_shapes_every_element(i):
+    """Seeded random draws: head dim, dtype, gradient dtype, causal, 1-3
+    batches of 1-4 heads, length log-uniform in 1 ... 500, logit spread, and
+    no key mask, a padding mask (random lengths, 0 and N included) or a
+    random non-contiguous one; every element against the oracle."""
+    c = RANDOM[i]
+    w = C[C3].with_shape(B=c["B"], H=c["H"], N=c["N"], d=c["d"], in_dtype=c["dtype"], out_dtype=c["dtype"],
+                         causal=c["causal"], q_dist=("normal", c["qk"]), k_dist=("normal", c["qk"]),
+                         key_padding=False, seed=c["seed"])
+    g = torch.Generator().manual_seed(c["seed"] + 1)
+    lens = None
+    if c["mask"] == "padding":
+        lens = torch.randint(0, c["N"] + 1, (c["B"],), generator=g, dtype=torch.int64)
+    x = W.generate(w, lens=lens)
+    if c["mask"] == "general":
+        x["mask"] = (torch.rand((c["B"], c["N"]), generator=g) < 0.6).to(torch.uint8)
+    do = W.generate_dout(w)
+    log(f"case bwd random {i}: {c}")
+    ref, o, lse = _oracle_inputs(x, do)
+    got = run_bwd(x, do, o, lse, None if c["grad"] == "same" else "f32")
+    dead_k = None
+    if x["mask"] is not None:
+        dead_k = np.broadcast_to((x["mask"].numpy() == 0)[:, None, :], ref["lse"].shape)
+    e = check(got, ref, c["dtype"], f"bwd random {i}", np.isneginf(ref["lse"]), dead_k)
+    log(f"  rel errors dq={e[0]:.2e} dk={e[1]:.2e} dv={e[2]:.2e}")
