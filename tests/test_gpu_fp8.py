@@ -181,3 +181,35 @@ def test_headline_fp8_workload_sampled_rows():
         worst.append(compare_fp8(O[b, h][rr], L[b, h][rr], ref, x["out_dtype"], 8, f"{BASE.name} head {bh}"))
     e = tuple(max(t[i] for t in worst) for i in range(3))
     U.log(f"  {BASE.name}: {len(rows)} rows, max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e} worst err/bound={e[2]:.2f}")
+
+
+def _draw(i):
+    r = np.random.default_rng(60000 + i)
+    return dict(causal=bool(r.integers(2)), B=int(r.integers(1, 4)), H=int(r.integers(1, 4)),
+                N=max(1, int(np.exp(r.uniform(0.0, np.log(400.0))))), out=["bf16", "f16", "f32"][int(r.integers(3))],
+                qk=float(r.choice([16.0, 32.0, 64.0])), offset=[8, 0][int(r.integers(2))],
+                mask=["none", "padding", "general"][int(r.integers(3))], seed=61000 + i)
+
+
+RANDOM = [_draw(i) for i in range(30)]
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM)))
+def test_random_shapes_every_row(i):
+    """Seeded random draws: causal or not, 1-3 batches of 1-3 heads, length
+    log-uniform in 1 ... 400, output dtype, stored logit spread (descale
+    2^-6), Max_offset 8 or 0, and no key mask, a padding mask (random
+    lengths) or a random non-contiguous one; every row against the oracle
+    within the per-row rounding bound."""
+    c = RANDOM[i]
+    w = BASE.with_shape(B=c["B"], H=c["H"], N=c["N"], causal=c["causal"], out_dtype=c["out"],
+                        q_dist=("normal", c["qk"]), k_dist=("normal", c["qk"]), seed=c["seed"])
+    g = torch.Generator().manual_seed(c["seed"] + 1)
+    lens = None
+    if c["mask"] == "padding":
+        lens = torch.randint(0, c["N"] + 1, (c["B"],), generator=g, dtype=torch.int64)
+    x = W.generate(w, lens=lens)
+    if c["mask"] == "general":
+        x["mask"] = (torch.rand((c["B"], c["N"]), generator=g) < 0.6).to(torch.uint8)
+    U.log(f"case fp8 random {i}: {c}")
+    check_all_rows(x, c["offset"], f"fp8 random {i}")
