@@ -54,6 +54,7 @@ struct BwdParams {
     int n_ktiles;          // dK/dV kernel: ceil(N / B_k)
     int xcd_remap;         // XcdMode: how workgroup ids spread over the 8 XCDs
     int head_group;        // heads whose tiles are dealt together (>= 1)
+    int n_dkdv_blocks;     // fused kernel: workgroups [0, n) are dK/dV, the rest dQ
     float c;               // scale * log2(e)
     float scale;
 };
@@ -121,8 +122,10 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dQ
 
+// The body takes its workgroup index and the number of workgroups that share
+// the work (the dQ kernel's grid, or its part of the fused grid below).
 template <int D, int BC, int NW, typename TI, typename TO, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int block, int grid) {
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BC % 32 == 0 && BC >= 32 && BC <= 64, "key tile");
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
     const int hh = lane >> 5;
 
     int split, bh, qt;  // workgroup -> (one key range, batch*head, query tile), as in the forward
-    schedule(blockIdx.x, gridDim.x, p.n_qtiles, p.B * p.H, 1, p.head_group, p.xcd_remap, &split, &bh, &qt);
+    schedule(block, grid, p.n_qtiles, p.B * p.H, 1, p.head_group, p.xcd_remap, &split, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;
     const int q0 = qt * BR;
@@ -367,12 +370,15 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
 #endif
 }
 
+template <int D, int BC, int NW, typename TI, typename TO, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
+    bwd_dq_body<D, BC, NW, TI, TO, CAUSAL, MASK>(p, blockIdx.x, gridDim.x);
+}
+
 // ---------------------------------------------------------------- dK, dV
 
-// At least two waves per SIMD: with K in LDS the kernel fits 256 registers.
 template <int D, int BQ, int NW, typename TI, typename TO, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_bwd_dkdv_kernel(
-    BwdParams p) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int block, int grid) {
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BQ == 32 || BQ == 64, "query tile");
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // the most queries, and they come first (work_item's order with the tile
     // index reversed).
     int split, bh, ktile;
-    schedule(blockIdx.x, gridDim.x, p.n_ktiles, p.B * p.H, 1, p.head_group, p.xcd_remap, &split, &bh, &ktile);
+    schedule(block, grid, p.n_ktiles, p.B * p.H, 1, p.head_group, p.xcd_remap, &split, &bh, &ktile);
     ktile = p.n_ktiles - 1 - ktile;
     const int b = bh / p.H;
     const int N = p.N;
@@ -647,6 +653,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
     }
 #endif
+}
+
+// At least two waves per SIMD: with K in LDS the kernel fits 256 registers.
+template <int D, int BQ, int NW, typename TI, typename TO, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_bwd_dkdv_kernel(
+    BwdParams p) {
+    bwd_dkdv_body<D, BQ, NW, TI, TO, CAUSAL, MASK>(p, blockIdx.x, gridDim.x);
+}
+
+// ---------------------------------------------------------------- dK, dV and dQ in one launch
+
+// Workgroups [0, n_dkdv_blocks) run the dK/dV body, the rest the dQ body;
+// the two are independent once the prep kernel has run. With both in one
+// grid the hardware starts dQ workgroups in the slots that the last round of
+// dK/dV workgroups leaves idle, instead of the dK/dV kernel ending on a
+// partly empty round and the dQ kernel on another. Used at d = 64, where the
+// two bodies' LDS together (about 50 KB) still leave three workgroups per CU;
+// at d = 128 it would leave one.
+template <int D, int BC, int BQ, int NW, typename TI, typename TO, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_fused_kernel(BwdParams p) {
+    const int nk = p.n_dkdv_blocks;
+    if ((int)blockIdx.x < nk) bwd_dkdv_body<D, BQ, NW, TI, TO, CAUSAL, MASK>(p, (int)blockIdx.x, nk);
+    else bwd_dq_body<D, BC, NW, TI, TO, CAUSAL, MASK>(p, (int)blockIdx.x - nk, (int)gridDim.x - nk);
 }
 
 }  // namespace fa

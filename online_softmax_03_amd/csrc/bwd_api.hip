@@ -1,5 +1,6 @@
 // Host side of fa_bwd (include/fa.h): argument validation, kernel choice and
-// the three launches (prep, dK/dV, dQ) on the caller's stream. No
+// the launches on the caller's stream: prep, then dK/dV and dQ (one fused
+// launch at d = 64, two at d = 128). No
 // allocation, no synchronisation, no state.
 #include <math.h>
 #include <stdint.h>
@@ -65,6 +66,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     const fa::BwdEntry* edq = find(fa::kBwdDq, d, in_dtype, grad_dtype, causal, key_padding_mask != nullptr);
     const fa::BwdEntry* ekv = find(fa::kBwdDkdv, d, in_dtype, grad_dtype, causal, key_padding_mask != nullptr);
     if (!prep || !edq || !ekv) return FA_ERR_TILE;
+    // d = 64: dK/dV and dQ in one launch (attn_bwd_fused_kernel)
+    const fa::BwdEntry* efu =
+        d == 64 ? find(fa::kBwdFused, d, in_dtype, grad_dtype, causal, key_padding_mask != nullptr) : nullptr;
 
     const long long bh = (long long)B * H;
     const long long n_g = groups(N);
@@ -73,7 +77,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     const long long prep_rows_per_block = 256 / (d / 8);
     const long long prep_grid = (bh * n_g * 32 + prep_rows_per_block - 1) / prep_rows_per_block;
     const long long grid = bh * n_qtiles;
-    if ((long long)N * d * 4 > INT32_MAX || grid > INT32_MAX || prep_grid > INT32_MAX) return FA_ERR_SHAPE;
+    if ((long long)N * d * 4 > INT32_MAX || 2 * grid > INT32_MAX || prep_grid > INT32_MAX) return FA_ERR_SHAPE;
 
     fa::BwdParams prm;
     prm.q = q;
@@ -95,12 +99,18 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     prm.n_ktiles = (int)n_ktiles;
     prm.xcd_remap = fa::xcd_mode_for(B * H, grid);
     prm.head_group = fa::head_group_for(B * H, causal);
+    prm.n_dkdv_blocks = (int)grid;
     prm.c = (float)((double)scale * 1.4426950408889634074);
     prm.scale = scale;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     void* args[] = {&prm};
     if (hipLaunchKernel(prep->fn, dim3((unsigned)prep_grid), dim3(256), args, 0, s) != hipSuccess)
         return FA_ERR_LAUNCH;
+    if (efu) {
+        if (hipLaunchKernel(efu->fn, dim3((unsigned)(2 * grid)), dim3(fa::kBwdNW * 64), args, 0, s) != hipSuccess)
+            return FA_ERR_LAUNCH;
+        return FA_OK;
+    }
     if (hipLaunchKernel(ekv->fn, dim3((unsigned)grid), dim3(fa::kBwdNW * 64), args, 0, s) != hipSuccess)
         return FA_ERR_LAUNCH;
     if (hipLaunchKernel(edq->fn, dim3((unsigned)grid), dim3(fa::kBwdNW * 64), args, 0, s) != hipSuccess)

@@ -13,7 +13,8 @@ constexpr int kBwdNW = 4;
 constexpr int kBwdBC = 32;
 constexpr int kBwdBQ = 32;
 
-enum { kBwdPrep = 0, kBwdDq = 1, kBwdDkdv = 2 };
+// kBwdFused: dK/dV and dQ in one launch (attn_bwd_fused_kernel; d = 64).
+enum { kBwdPrep = 0, kBwdDq = 1, kBwdDkdv = 2, kBwdFused = 3 };
 
 struct BwdEntry {
     int kind, d, in_dtype, out_dtype, causal, mask;

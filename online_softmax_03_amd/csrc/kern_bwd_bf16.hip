@@ -10,6 +10,13 @@
         fa::BwdEntry{fa::kBwdDkdv, D, IN, OUT, C, M,                                                        \
                      reinterpret_cast<const void*>(&fa::attn_bwd_dkdv_kernel<D, fa::kBwdBQ, fa::kBwdNW, fa::TI, \
                                                                              fa::TO, (C) != 0, (M) != 0>)}
+#define FA_BWD_FUSED(D, TI, IN, TO, OUT, C, M)                                                               \
+    fa::BwdEntry{fa::kBwdFused, D, IN, OUT, C, M,                                                           \
+                 reinterpret_cast<const void*>(&fa::attn_bwd_fused_kernel<D, fa::kBwdBC, fa::kBwdBQ, fa::kBwdNW,   \
+                                                                          fa::TI, fa::TO, (C) != 0, (M) != 0>)}
+#define FA_BWD_FUSED_FLAGS(D, TI, IN, TO, OUT)                                            \
+    FA_BWD_FUSED(D, TI, IN, TO, OUT, 0, 0), FA_BWD_FUSED(D, TI, IN, TO, OUT, 0, 1),      \
+        FA_BWD_FUSED(D, TI, IN, TO, OUT, 1, 0), FA_BWD_FUSED(D, TI, IN, TO, OUT, 1, 1)
 #define FA_BWD_FLAGS(D, TI, IN, TO, OUT)                                                  \
     FA_BWD_PAIR(D, TI, IN, TO, OUT, 0, 0), FA_BWD_PAIR(D, TI, IN, TO, OUT, 0, 1),        \
         FA_BWD_PAIR(D, TI, IN, TO, OUT, 1, 0), FA_BWD_PAIR(D, TI, IN, TO, OUT, 1, 1)
@@ -18,7 +25,8 @@
         fa::BwdEntry{fa::kBwdPrep, 128, IN, -1, 0, 0,                                                      \
                      reinterpret_cast<const void*>(&fa::attn_bwd_prep_kernel<128, fa::TI>)},               \
         FA_BWD_FLAGS(64, TI, IN, TI, IN), FA_BWD_FLAGS(64, TI, IN, F32, FA_DTYPE_F32),                     \
-        FA_BWD_FLAGS(128, TI, IN, TI, IN), FA_BWD_FLAGS(128, TI, IN, F32, FA_DTYPE_F32)
+        FA_BWD_FLAGS(128, TI, IN, TI, IN), FA_BWD_FLAGS(128, TI, IN, F32, FA_DTYPE_F32),                  \
+        FA_BWD_FUSED_FLAGS(64, TI, IN, TI, IN), FA_BWD_FUSED_FLAGS(64, TI, IN, F32, FA_DTYPE_F32)
 
 namespace fa {
 static const BwdEntry kBwdEntries_bf16[] = {FA_BWD_DTYPE(BF16, FA_DTYPE_BF16)};
