@@ -270,7 +270,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N);
  *   workspace device memory of at least fa_bwd_workspace_bytes(B, H, N)
  *             bytes, 16-byte aligned, owned by the caller, overwritten
  *   stream    hipStream_t, or NULL
- * Enqueues three kernels (per-row D and LSE, then dK/dV, then dQ). Calls
+ * Enqueues the per-row D and LSE kernel, then dK/dV and dQ (two kernels at
+ * d = 128, one launch holding both at d = 64). Calls
  * that share a workspace must be ordered on the device. Returns FA_OK or a
  * negative fa_status; nothing is launched on error.
  */

@@ -10,7 +10,8 @@
 //   dK = scale dS^T Q,
 //
 // the chain rule through P V and through the row softmax. Three kernels, on
-// the caller's stream in this order:
+// the caller's stream in this order (at d = 64 the last two run as one
+// launch, attn_bwd_fused_kernel below):
 //
 //   attn_bwd_prep_kernel  D_i and LSE_i * log2(e) for every query, written to
 //     a workspace laid out in groups of 32 queries, [lse2 x 32][D x 32] per
