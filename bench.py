@@ -156,8 +156,10 @@ def traffic(workload, kernel=KERNEL_PREFIX, tile=None):
 class ClockSampler:
     """Reads the GPU's shader clock from the SMU metrics table through amdsmi
     (current_gfxclk, MHz) in a background thread while `active`. The table
-    is refreshed about once a second, so only readings whose table timestamp
-    changed after the sampler started count; a shorter run gets none."""
+    is refreshed about once a second and its clock is an average over the
+    period before the refresh, so the first refresh after the sampler
+    starts still covers time before the load: only the readings of later
+    refreshes count, and a run shorter than two refresh periods gets none."""
 
     def __init__(self, period_s=0.005):
         self.period_s = period_s
@@ -191,12 +193,15 @@ class ClockSampler:
 
     def _loop(self):
         last = self._start_stamp
+        refreshes = 0
         while not self._stop:
             if self.active:
                 try:
                     stamp, mhz = self._read()
                     if stamp != last:
-                        self.samples.append(mhz)
+                        refreshes += 1
+                        if refreshes >= 2:
+                            self.samples.append(mhz)
                         last = stamp
                 except Exception:
                     pass
