@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "work_item.h"
 
 namespace fa {
@@ -134,25 +136,21 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt(0xC07F);
 }
 
-template <typename T>
-__device__ __forceinline__ void store_row4(char* dst, const float* v4, float inv);
-
-template <>
-__device__ __forceinline__ void store_row4<F32>(char* dst, const float* v4, float inv) {
-    f32x4 r = {v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
-    *reinterpret_cast<f32x4*>(dst) = r;
-}
-
-template <>
-__device__ __forceinline__ void store_row4<BF16>(char* dst, const float* v4, float inv) {
-    u32x2 r = {pack2<BF16>(v4[0] * inv, v4[1] * inv), pack2<BF16>(v4[2] * inv, v4[3] * inv)};
-    *reinterpret_cast<u32x2*>(dst) = r;
-}
-
-template <>
-__device__ __forceinline__ void store_row4<F16>(char* dst, const float* v4, float inv) {
-    u32x2 r = {pack2<F16>(v4[0] * inv, v4[1] * inv), pack2<F16>(v4[2] * inv, v4[3] * inv)};
-    *reinterpret_cast<u32x2*>(dst) = r;
+// Four consecutive values of an output row, times `inv`, in the output type
+// (16 bytes for fp32, 8 for bf16/fp16, rounded to nearest even). NT marks the
+// store non-temporal (the `nt` hint): a final output that the launch does not
+// read back, written in one burst as the workgroups finish.
+template <typename T, bool NT = false>
+__device__ __forceinline__ void store_row4(char* dst, const float* v4, float inv) {
+    if constexpr (std::is_same_v<T, F32>) {
+        const f32x4 r = {v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
+        if constexpr (NT) __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(dst));
+        else *reinterpret_cast<f32x4*>(dst) = r;
+    } else {
+        const u32x2 r = {pack2<T>(v4[0] * inv, v4[1] * inv), pack2<T>(v4[2] * inv, v4[3] * inv)};
+        if constexpr (NT) __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(dst));
+        else *reinterpret_cast<u32x2*>(dst) = r;
+    }
 }
 
 // Valid-key extent of one mask row over [0, n): the first and last index
