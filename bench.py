@@ -252,26 +252,44 @@ def settle(step, settle_ms):
 
 
 def timed_steps(step, stream, steps, warmup, clock=None):
-    """Runs `warmup` untimed steps, then `steps` timed ones with a HIP event
-    pair around each on `stream`. Returns (wall seconds, per-launch ms list).
-    `clock` (a ClockSampler) stops sampling when the timed steps end."""
+    """Runs `warmup` untimed steps, then `steps` timed ones back to back with
+    one HIP event pair on `stream` around all of them. Returns (wall seconds,
+    average ms per step by the events). An event pair around every launch
+    would add its own ~6 us of wall time to each step (the next launch waits
+    for the end-of-kernel timestamp): 0.5% of the default step, 7% of a
+    90 us d = 64 step. `clock` (a ClockSampler) stops sampling when the
+    timed steps end."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    a.record(stream)
+    for _ in range(steps):
         step()
-        ends[i].record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if clock is not None:
         clock.active = False
-    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, a.elapsed_time(b) / steps
+
+
+def per_launch(step, stream, n):
+    """`n` more launches after the timed ones, each inside its own HIP event
+    pair on `stream` (median and minimum per launch; not part of `value`)."""
+    import torch
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
 
 
 def flushed_launches(step, stream, n, flush_mib):
@@ -348,9 +366,10 @@ def bench_softmax(args):
     clock = ClockSampler()
     clock.active = True
     settled = settle(step, args.settle_ms) if args.settle_ms > 0 else 0
-    wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup, clock)
+    wall, avg_ms = timed_steps(step, stream, args.steps, args.warmup, clock)
     clock.close()
-    avg_s = sum(launch_ms) / len(launch_ms) / 1e3
+    launch_ms = per_launch(step, stream, args.steps)
+    avg_s = avg_ms / 1e3
     nbytes = w.algorithmic_bytes()
     # the library's choice: registers (up to 8192 16-byte vectors), registers
     # + LDS (up to 20480 vectors for 16-bit inputs, 32768 for fp32), streamed
@@ -463,14 +482,16 @@ def main():
             A.attention_fwd(q, k, v, scale=w.scale, causal=w.causal, key_padding_mask=mask,
                             out_dtype=out_dt, out=o, lse=lse, num_splits=splits, workspace=ws)
 
-    # the GPU leaves its idle clock first; then per-launch HIP events on the
-    # stream the kernel is launched on, with the shader clock sampled alongside
+    # the GPU leaves its idle clock first; then the timed steps inside one HIP
+    # event pair on the stream the kernel is launched on, with the shader
+    # clock sampled alongside
     clock = ClockSampler()
     clock.active = True
     settled = settle(step, args.settle_ms) if args.settle_ms > 0 else 0
-    wall, launch_ms = timed_steps(step, stream, args.steps, args.warmup, clock)
+    wall, avg_ms = timed_steps(step, stream, args.steps, args.warmup, clock)
     clock.close()
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    launch_ms = per_launch(step, stream, args.steps)
+    avg_launch_s = avg_ms / 1e3
     flushed = flushed_launches(step, stream, 5, args.flush_mib) if args.flush_mib > 0 else None
 
     flops = w.nominal_flops() * (2.5 if args.bwd else 1.0)

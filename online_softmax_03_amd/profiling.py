@@ -180,7 +180,7 @@ def _report(a) -> None:
                      f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} | {float(r['Percentage']):.1f}% |")
     rf = bench["roofline"]
     lines += ["", "## bench.py line of the same run", "", "```json", json.dumps(bench, indent=1), "```", "",
-              f"bench.py's own per-launch HIP-event average: {rf['avg_launch_ms']:.4f} ms; "
+              f"bench.py's own HIP-event average over the timed launches: {rf['avg_launch_ms']:.4f} ms; "
               f"achieved {rf['achieved']} {rf['unit']} = {100 * rf['frac']:.1f}% of {rf['peak']} {rf['unit']}."]
     if a.traffic and os.path.exists(a.traffic):
         with open(a.traffic) as fh:
