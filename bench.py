@@ -454,7 +454,7 @@ def main():
         if args.tile:
             sys.exit("--num-splits uses the default tile; drop --tile")
         if splits == 0:
-            splits = capi.fa_splitkv_num_splits(w.B, w.H, w.N, w.d, A._DT[q.dtype])
+            splits = capi.fa_splitkv_num_splits(w.B, w.H, w.N, w.d, A._DT[q.dtype], w.causal)
         ws = torch.empty(capi.fa_splitkv_workspace_bytes(w.B, w.H, w.N, w.d, splits), dtype=torch.uint8,
                          device=dev)
 

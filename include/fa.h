@@ -143,6 +143,12 @@ int fa_tile_supported(int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype, const fa
  * fill the device (small batch, few heads, short N): each part is one more
  * workgroup. The result matches fa_fwd to rounding; only the order of the
  * float32 additions differs.
+ *
+ * Every query tile's keys are cut into num_splits parts, except under a
+ * causal mask with 16-bit inputs when B * H * ceil(N / block_r) <= 256: there
+ * query tile t sees (t + 1) * block_r keys and gets parts in proportion, each
+ * of at most u * block_r keys for the smallest u that leaves the last tile at
+ * most num_splits parts, so that every workgroup has about the same work.
  */
 
 /* fa_splitkv_workspace_bytes — bytes of device workspace fa_fwd_splitkv needs:
@@ -151,13 +157,18 @@ int fa_tile_supported(int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype, const fa
  * (same rules as fa_fwd_splitkv). Host only, no HIP call. */
 size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
 
-/* fa_splitkv_num_splits — a split count for these sizes: the smallest count
- * whose workgroups fill every slot of the 256 compute units at once (3
- * resident workgroups per CU for the 16-bit d = 128 kernel, 2 for the 16-bit
- * d = 64 kernel and fp32 inputs at d = 64, 1 for fp32 inputs at d = 128), capped so that every part keeps at least four key tiles (one
- * for fp32 inputs) and at 8 parts. Returns the count (1..8) or a negative
- * fa_status. Host only, no HIP call. */
-int fa_splitkv_num_splits(int B, int H, int N, int d, fa_dtype_t in_dtype);
+/* fa_splitkv_num_splits — a split count for these sizes and mask. With
+ * equal parts per query tile: the smallest count whose workgroups fill every
+ * slot of the 256 compute units at once (3 resident workgroups per CU for the
+ * 16-bit d = 128 kernel, 2 for the 16-bit d = 64 kernel and fp32 inputs at
+ * d = 64, 1 for fp32 inputs at d = 128), capped so that every part keeps at
+ * least four key tiles (one for fp32 inputs) and at 8 parts. With parts in
+ * proportion to the causal extent (causal != 0, 16-bit inputs, at most 256
+ * query tiles; see fa_fwd_splitkv): the smallest count whose workgroups reach
+ * 9/16 of those slots, capped at 12 and at four key tiles per part of the
+ * longest query tile. Returns the count (1..12) or a negative fa_status.
+ * Host only, no HIP call. */
+int fa_splitkv_num_splits(int B, int H, int N, int d, fa_dtype_t in_dtype, int causal);
 
 /*
  * fa_fwd_splitkv — attention forward with the keys split into num_splits

@@ -71,7 +71,7 @@ def attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: floa
         if tile is not None:
             raise ValueError("the split-KV path uses the default tile")
         if num_splits == 0:
-            num_splits = capi.fa_splitkv_num_splits(B, H, N, d, _DT[q.dtype])
+            num_splits = capi.fa_splitkv_num_splits(B, H, N, d, _DT[q.dtype], causal)
             if num_splits < 0:
                 raise FaError(num_splits)
         need = capi.fa_splitkv_workspace_bytes(B, H, N, d, num_splits)

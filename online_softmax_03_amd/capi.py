@@ -73,7 +73,7 @@ def library():
             lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
             lib.fa_splitkv_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
             lib.fa_splitkv_num_splits.restype = _I
-            lib.fa_splitkv_num_splits.argtypes = [_I, _I, _I, _I, _I]
+            lib.fa_splitkv_num_splits.argtypes = [_I, _I, _I, _I, _I, _I]
             lib.fa_fwd_splitkv.restype = _I
             lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:-1] + [_I, _P, ctypes.c_size_t, _P]
             lib.fa_fwd_splitkv_noalloc.restype = _I
@@ -125,8 +125,8 @@ def fa_splitkv_workspace_bytes(B, H, N, d, num_splits) -> int:
     return int(library().fa_splitkv_workspace_bytes(B, H, N, d, num_splits))
 
 
-def fa_splitkv_num_splits(B, H, N, d, in_dtype) -> int:
-    return library().fa_splitkv_num_splits(B, H, N, d, in_dtype)
+def fa_splitkv_num_splits(B, H, N, d, in_dtype, causal) -> int:
+    return library().fa_splitkv_num_splits(B, H, N, d, in_dtype, int(causal))
 
 
 def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask, in_dtype, out_dtype,

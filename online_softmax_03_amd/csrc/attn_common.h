@@ -44,12 +44,35 @@ struct Params {
     int fair;             // 1: equal-progress wave priorities (see fa_api.hip)
     float c;              // scale * log2(e)
     // split-KV only: the key tiles of every query tile are cut into n_splits
-    // contiguous parts; part s writes its normalised partial output and its
-    // LSE to ws_o [n_splits][B*H][N][d] and ws_lse [n_splits][B*H][N].
+    // contiguous parts (with split_u > 0, under a causal mask: parts_of(...)
+    // <= n_splits parts of at most split_u * B_r / B_c key tiles each,
+    // work_item.h, split_parts = parts_per_head workgroups per head); part s
+    // writes its normalised partial output and its LSE to ws_o
+    // [n_splits][B*H][N][d] and ws_lse [n_splits][B*H][N].
     int n_splits;
+    int split_u;
+    long long split_parts;
     float* ws_o;
     float* ws_lse;
 };
+
+// Workgroup -> (key-range part `split` of `n_parts`, batch*head `bh`, query
+// tile `qt`) for the attention kernels (work_item.h).
+template <bool SPLIT, bool CAUSAL>
+__device__ __forceinline__ void attn_schedule(const Params& p, int* split, int* n_parts, int* bh, int* qt) {
+    if constexpr (SPLIT && CAUSAL) {
+        if (p.split_u > 0) {
+            long long k = 0;
+            schedule_parts((int)blockIdx.x, (int)gridDim.x, p.split_parts, p.xcd_remap, bh, &k);
+            locate_part(k, p.n_qtiles, p.split_u, p.n_splits, qt, split);
+            *n_parts = parts_of(*qt, p.n_qtiles, p.split_u, p.n_splits);
+            return;
+        }
+    }
+    *n_parts = SPLIT ? p.n_splits : 1;
+    schedule((int)blockIdx.x, (int)gridDim.x, p.n_qtiles, p.B * p.H, *n_parts, p.head_group, p.xcd_remap, split,
+             bh, qt);
+}
 
 constexpr float kLn2 = 0.69314718055994530942f;
 // Largest growth of a row maximum, in log2 units of the exponent, tolerated

@@ -101,10 +101,10 @@ void attn_fwd_kernel(Params p) {
     // workgroup -> (key-range part, batch*head, query tile): every tile of a
     // head runs on one XCD, so the workgroups sharing its K/V share an L2, and
     // each XCD starts its longest tiles (largest causal extent) first
-    // (schedule, work_item.h).
-    int split, bh, qt;
-    schedule(blockIdx.x, gridDim.x, p.n_qtiles, p.B * p.H, SPLIT ? p.n_splits : 1, p.head_group, p.xcd_remap,
-             &split, &bh, &qt);
+    // (schedule, work_item.h; causal split launches give every part about the
+    // same number of key tiles, schedule_parts / locate_part).
+    int split, n_parts, bh, qt;
+    attn_schedule<SPLIT, CAUSAL>(p, &split, &n_parts, &bh, &qt);
     const int b = bh / p.H;
     const int N = p.N;
     const int q0 = qt * BR;
@@ -138,7 +138,7 @@ void attn_fwd_kernel(Params p) {
     int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + BC - 1) / BC : 0;
     if constexpr (SPLIT) {
         // this workgroup's part of the key tiles: [t0, t1) of n_tiles
-        const int per = (n_tiles + p.n_splits - 1) / p.n_splits;
+        const int per = (n_tiles + n_parts - 1) / n_parts;
         const int t0 = min(n_tiles, split * per);
         const int t1 = min(n_tiles, t0 + per);
         kv_begin += t0 * BC;

@@ -25,6 +25,10 @@ struct MergeParams {
     float* lse;           // [rows]
     long long rows;       // B * H * N
     int n_splits;
+    // causal split launches (split_u > 0): the row's query tile (rows of N
+    // per head, block_r per tile, n_qtiles per head) has parts_of(...) parts
+    int split_u;
+    int N, block_r, n_qtiles;
 };
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -36,7 +40,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
     const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
     const int t = threadIdx.x % TPR;
     if (row >= mp.rows) return;
-    const int S = mp.n_splits;
+    const int S = mp.split_u > 0
+                      ? parts_of((int)(row % mp.N) / mp.block_r, mp.n_qtiles, mp.split_u, mp.n_splits)
+                      : mp.n_splits;
     float M = -INFINITY;
     for (int s = 0; s < S; ++s) M = fmaxf(M, mp.ws_lse[(long long)s * mp.rows + row]);
     float o[4] = {0.f, 0.f, 0.f, 0.f};

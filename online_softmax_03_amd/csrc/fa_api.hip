@@ -86,6 +86,37 @@ size_t splitkv_bytes(int B, int H, int N, int d, int S) {
     return (size_t)S * (size_t)rows * (size_t)(d + 1) * sizeof(float);
 }
 
+// The parts of a split-KV launch with the default tile. Under a causal mask,
+// for 16-bit inputs, when the unsplit launch has no more query tiles than
+// there are CUs (B*H*ceil(N/block_r) <= 256), query tile qt gets parts in
+// proportion to its causal extent: at most u * block_r / block_c key tiles
+// each, num_splits (at most) for the last tile (parts_of, work_item.h). Every
+// query tile otherwise gets num_splits parts. Same-box comparisons on causal
+// d = 128, N = 8192 (TFLOP/s, equal parts against proportional parts, at the
+// best part count of each): 1 head 369 / 418, 2 heads 454 / 584, 4 heads 630
+// / 691; 8 heads 866 / 786 (512 query tiles: equal parts, 1024 workgroups of
+// all lengths, fill the slots better than 768 equal ones) and 8 heads at
+// N = 4096 (256 query tiles) 576 / 568.
+struct SplitPlan {
+    int u;             // 0: num_splits equal parts for every query tile
+    int s_last;        // parts of the longest query tile (<= num_splits)
+    long long parts;   // workgroups per head
+};
+
+SplitPlan split_plan(int B, int H, int N, int d, int in_dtype, int causal, int num_splits) {
+    const fa_tile t = default_tile(d, in_dtype);
+    const long long n_qtiles = ((long long)N + t.block_r - 1) / t.block_r;
+    SplitPlan sp{0, num_splits, n_qtiles * num_splits};
+    if (causal && in_dtype != FA_DTYPE_F32 && (long long)B * H * n_qtiles <= 256) {
+        const int r = t.block_r / t.block_c;
+        const int n_k = (N + t.block_c - 1) / t.block_c;
+        sp.u = fa::split_unit(n_k, r, num_splits);
+        sp.s_last = (n_k + sp.u * r - 1) / (sp.u * r);
+        sp.parts = fa::parts_per_head((int)n_qtiles, sp.u, sp.s_last);
+    }
+    return sp;
+}
+
 // Shared argument checks of fa_fwd_ex and fa_fwd_splitkv.
 int check_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
                  int d, float scale, int in_dtype, int out_dtype) {
@@ -117,6 +148,8 @@ void fill_params(fa::Params& prm, const void* q, const void* k, const void* v, v
     prm.fair = 0;
     prm.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
     prm.n_splits = 1;
+    prm.split_u = 0;
+    prm.split_parts = 0;
     prm.ws_o = nullptr;
     prm.ws_lse = nullptr;
 }
@@ -165,7 +198,10 @@ int launch_splitkv(const void* q, const void* k, const void* v, void* o, float* 
     if (!e || !me) return FA_ERR_TILE;
     const long long rows = (long long)B * H * N;
     const long long n_qtiles = ((long long)N + t.block_r - 1) / t.block_r;
-    const long long grid = (long long)B * H * n_qtiles * num_splits;
+    const SplitPlan sp = split_plan(B, H, N, d, in_dtype, causal, num_splits);
+    const int u = sp.u, s_last = sp.s_last;
+    const long long parts = sp.parts;
+    const long long grid = (long long)B * H * parts;
     const long long rows_per_block = 256 / (d / 4);
     const long long merge_grid = (rows + rows_per_block - 1) / rows_per_block;
 
@@ -173,7 +209,9 @@ int launch_splitkv(const void* q, const void* k, const void* v, void* o, float* 
     float* ws_lse = ws_o + (size_t)num_splits * (size_t)rows * (size_t)d;
     fa::Params prm;
     fill_params(prm, q, k, v, o, lse, key_padding_mask, B, H, N, scale, causal, n_qtiles, grid);
-    prm.n_splits = num_splits;
+    prm.n_splits = s_last;
+    prm.split_u = u;
+    prm.split_parts = parts;
     prm.ws_o = ws_o;
     prm.ws_lse = ws_lse;
     void* args[] = {&prm};
@@ -185,7 +223,11 @@ int launch_splitkv(const void* q, const void* k, const void* v, void* o, float* 
     mp.o = o;
     mp.lse = lse;
     mp.rows = rows;
-    mp.n_splits = num_splits;
+    mp.n_splits = s_last;
+    mp.split_u = u;
+    mp.N = N;
+    mp.block_r = t.block_r;
+    mp.n_qtiles = (int)n_qtiles;
     void* margs[] = {&mp};
     if (hipLaunchKernel(me->fn, dim3((unsigned)merge_grid), dim3(256), margs, 0, s) != hipSuccess)
         return FA_ERR_LAUNCH;
@@ -262,13 +304,27 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
     return splitkv_bytes(B, H, N, d, num_splits);
 }
 
-int fa_splitkv_num_splits(int B, int H, int N, int d, fa_dtype_t in_dtype) {
+int fa_splitkv_num_splits(int B, int H, int N, int d, fa_dtype_t in_dtype, int causal) {
     if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
     if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16 && in_dtype != FA_DTYPE_F16) return FA_ERR_DTYPE;
     const fa_tile t = default_tile(d, in_dtype);
     const long long grid = (long long)B * H * (((long long)N + t.block_r - 1) / t.block_r);
     const long long key_tiles = ((long long)N + t.block_c - 1) / t.block_c;
+    if (split_plan(B, H, N, d, in_dtype, causal, 1).u > 0) {
+        // Causal parts in proportion to the keys: the smallest count whose
+        // workgroups reach 9/16 of the slots, at most 12, with at least four
+        // key tiles per part of the longest query tile. Same-box sweeps of
+        // 2 .. 24 on causal d = 128, N = 8192: the best counts were 6 - 12
+        // for 1 head (219 - 374 workgroups), 6 for 2 heads (438), 3 for 4
+        // heads (504); more parts than that lost 10 - 25%.
+        const long long target = 256LL * resident_wgs_per_cu(d, in_dtype) * 9 / 16;
+        int s = 1;
+        while (s < 12 && key_tiles / (s + 1) >= 4 &&
+               (long long)B * H * split_plan(B, H, N, d, in_dtype, causal, s).parts < target)
+            ++s;
+        return s;
+    }
     // Enough parts to fill every workgroup slot of the 256 CUs at once,
     // keeping at least four key tiles per part and at most 8 parts (beyond
     // that the merge, which reads every part's row, costs more than the

@@ -64,6 +64,73 @@ constexpr void schedule(int block, int grid, int n_tiles, int n_heads, int n_spl
     work_item(id, n_tiles, n_heads, G, bh, tile);
 }
 
+// Split-KV parts under a causal mask. Query tile qt of n_q (B_r rows each)
+// sees r*(qt+1) key tiles of B_c keys (r = B_r / B_c), the last one all n_k
+// of them, so equal part counts per query tile would give the parts of the
+// last tiles the most keys and the launch would wait for them. Instead each
+// part gets at most u*r key tiles: query tile qt < n_q - 1 has
+// ceil((qt+1)/u) parts and the last one s_last = ceil(n_k / (u*r)), the
+// most of any tile (the caller's part count). parts_of gives a tile's
+// count, parts_before the sum over the tiles before it,
+// sum_{j=1..qt} ceil(j/u) = u*Q*(Q+1)/2 + R*(Q+1) with qt = Q*u + R.
+constexpr int parts_of(int qt, int n_q, int u, int s_last) {
+    return qt < n_q - 1 ? (qt + u) / u : s_last;
+}
+
+constexpr long long parts_before(int qt, int u) {
+    const long long Q = qt / u, R = qt - Q * u;
+    return (long long)u * Q * (Q + 1) / 2 + R * (Q + 1);
+}
+
+constexpr long long parts_per_head(int n_q, int u, int s_last) { return parts_before(n_q - 1, u) + s_last; }
+
+// Part k of a head (0 <= k < parts_per_head) -> query tile `qt` and its part
+// `s`, by a binary search over parts_before (increasing in qt).
+constexpr void locate_part(long long k, int n_q, int u, int s_last, int* qt, int* s) {
+    const long long last0 = parts_before(n_q - 1, u);
+    if (k >= last0) {
+        *qt = n_q - 1;
+        *s = (int)(k - last0);
+        return;
+    }
+    int lo = 0, hi = n_q - 2;  // the largest q with parts_before(q) <= k
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (parts_before(mid, u) <= k) lo = mid;
+        else hi = mid - 1;
+    }
+    *qt = lo;
+    *s = (int)(k - parts_before(lo, u));
+}
+
+// Workgroup `block` of a causal split launch (n_heads * P workgroups, P =
+// parts_per_head) -> (batch*head `bh`, part `k` of that head), by the XCD
+// modes above; each head's parts run from the last (those of the last query
+// tile) to the first.
+constexpr void schedule_parts(int block, int grid, long long P, int xcd_mode, int* bh, long long* k) {
+    long long id = 0;
+    if (xcd_mode == kXcdHeads) {
+        const long long j = block >> 3;  // the j-th item of XCD block % 8
+        *bh = (int)(j / P) * 8 + (block & 7);
+        id = j % P;
+    } else {
+        long long b = block;
+        if (xcd_mode == kXcdChunks) b = (long long)(block & 7) * (grid >> 3) + (block >> 3);
+        *bh = (int)(b / P);
+        id = b % P;
+    }
+    *k = P - 1 - id;
+}
+
+// Host side: u for a causal split launch whose longest query tile (n_k key
+// tiles) gets at most `num_splits` parts, r = B_r / B_c: the smallest u with
+// ceil(n_k / (u*r)) <= num_splits.
+constexpr int split_unit(int n_k, int r, int num_splits) {
+    const int per = (n_k + num_splits - 1) / num_splits;  // key tiles per part, at least
+    const int u = (per + r - 1) / r;
+    return u < 1 ? 1 : u;
+}
+
 // Host side: the XCD mode of a launch over n_heads heads and `grid`
 // workgroups.
 constexpr int xcd_mode_for(int n_heads, long long grid) {

@@ -39,7 +39,7 @@ def run_gpu(x: dict, tile=None, canary=True, num_splits=None):
     ws = None
     if num_splits is not None:
         B, H, N, d = q.shape
-        s = num_splits or A.capi.fa_splitkv_num_splits(B, H, N, d, A._DT[q.dtype])
+        s = num_splits or A.capi.fa_splitkv_num_splits(B, H, N, d, A._DT[q.dtype], x["causal"])
         ws = torch.full((A.capi.fa_splitkv_workspace_bytes(B, H, N, d, s),), 0xFF, dtype=torch.uint8, device=dev)
         num_splits = s
     A.attention_fwd(q, k, v, scale=x["scale"], causal=x["causal"], key_padding_mask=mask,

@@ -76,13 +76,16 @@ int main(void) {
     EXPECT(fa_splitkv_workspace_bytes(1, 1, 8, 64, FA_MAX_SPLITS + 1), 0);
     for (int n = 1; n <= (1 << 20); n *= 3)
         for (int h = 1; h <= 64; h *= 4) {
-            const int a = fa_splitkv_num_splits(1, h, n, 128, BF);
-            const int b = fa_splitkv_num_splits(2, h, n, 64, F16);
-            const int c = fa_splitkv_num_splits(1, h, n, 128, F32);
-            EXPECT(a >= 1 && a <= 8 && b >= 1 && b <= 8 && c >= 1 && c <= 8, 1);
+            for (int causal = 0; causal < 2; ++causal) {
+                const int a = fa_splitkv_num_splits(1, h, n, 128, BF, causal);
+                const int b = fa_splitkv_num_splits(2, h, n, 64, F16, causal);
+                const int c = fa_splitkv_num_splits(1, h, n, 128, F32, causal);
+                EXPECT(a >= 1 && a <= 12 && b >= 1 && b <= 12 && c >= 1 && c <= 8, 1);
+            }
         }
-    EXPECT(fa_splitkv_num_splits(1, 1, 64, 80, BF), FA_ERR_HEADDIM);
-    EXPECT(fa_splitkv_num_splits(65536, 65536, 65536, 64, BF) >= 1, 1);
+    EXPECT(fa_splitkv_num_splits(1, 1, 64, 80, BF, 0), FA_ERR_HEADDIM);
+    EXPECT(fa_splitkv_num_splits(65536, 65536, 65536, 64, BF, 0) >= 1, 1);
+    EXPECT(fa_splitkv_num_splits(65536, 65536, 65536, 64, BF, 1) >= 1, 1);
     EXPECT(fa_fwd_splitkv(P, P, P, P, L, 1, 1, 128, 128, 0.1f, 0, NULL, BF, BF, 0, P, 1 << 20, s), FA_ERR_SPLITS);
     EXPECT(fa_fwd_splitkv(P, P, P, P, L, 1, 1, 128, 128, 0.1f, 0, NULL, BF, BF, 2, NULL, 1 << 20, s),
            FA_ERR_WORKSPACE);

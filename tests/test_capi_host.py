@@ -102,32 +102,45 @@ def test_splitkv_workspace_bytes():
 
 
 def test_splitkv_num_splits_heuristic():
-    # a full grid needs no split; a small one splits until its parts fill the
-    # 768 (d = 128, 16-bit) or 512 (d = 64) resident workgroup slots, keeping
-    # at least four key tiles per part, and into at most 8 parts
-    assert capi.fa_splitkv_num_splits(2, 32, 8192, 128, BF16) == 1
-    assert capi.fa_splitkv_num_splits(1, 16, 8192, 128, BF16) == 1   # 1024 workgroups
-    assert capi.fa_splitkv_num_splits(1, 8, 8192, 128, BF16) == 2    # 512 -> 1024
-    assert capi.fa_splitkv_num_splits(1, 4, 8192, 128, BF16) == 3    # 256 -> 768
-    assert capi.fa_splitkv_num_splits(1, 2, 8192, 128, BF16) == 6    # 128 -> 768
-    assert capi.fa_splitkv_num_splits(1, 8, 2048, 64, BF16) == 8     # 64 -> 512 (32 key tiles / 8)
-    assert capi.fa_splitkv_num_splits(1, 1, 8192, 128, BF16) == 8    # 64 -> 512: at most 8 parts
-    assert capi.fa_splitkv_num_splits(1, 1, 2048, 64, BF16) == 8     # capped: 32 key tiles, 4 per part
+    # equal parts per query tile: a full grid needs no split; a small one
+    # splits until its parts fill the 768 (d = 128, 16-bit) or 512 (d = 64)
+    # resident workgroup slots, keeping at least four key tiles per part, and
+    # into at most 8 parts
+    n = capi.fa_splitkv_num_splits
+    assert n(2, 32, 8192, 128, BF16, 0) == 1
+    assert n(1, 16, 8192, 128, BF16, 0) == 1   # 1024 workgroups
+    assert n(1, 8, 8192, 128, BF16, 0) == 2    # 512 -> 1024
+    assert n(1, 4, 8192, 128, BF16, 0) == 3    # 256 -> 768
+    assert n(1, 2, 8192, 128, BF16, 0) == 6    # 128 -> 768
+    assert n(1, 8, 2048, 64, BF16, 0) == 8     # 64 -> 512 (32 key tiles / 8)
+    assert n(1, 1, 8192, 128, BF16, 0) == 8    # 64 -> 512: at most 8 parts
+    assert n(1, 1, 2048, 64, BF16, 0) == 8     # capped: 32 key tiles, 4 per part
     for B, H, N, d in [(1, 2, 4096, 128), (1, 1, 8192, 128), (3, 5, 1000, 64), (1, 1, 300, 128)]:
-        s = capi.fa_splitkv_num_splits(B, H, N, d, BF16)
+        s = n(B, H, N, d, BF16, 0)
         br, bc, slots = (128, 32, 768) if d == 128 else (256, 64, 512)
         grid, tiles = B * H * -(-N // br), -(-N // bc)
         assert 1 <= s <= 8
         assert s == 1 or tiles // s >= 4                       # every part keeps four key tiles
         assert grid * s >= slots or s == 8 or tiles // (s + 1) < 4   # and no fewer parts would do
         assert s == 1 or grid * (s - 1) < slots
-    assert capi.fa_splitkv_num_splits(1, 1, 64, 128, BF16) == 1  # too few key tiles to split
+    assert n(1, 1, 64, 128, BF16, 0) == 1  # too few key tiles to split
+    # causal, at most 256 query tiles: parts in proportion to the causal
+    # extent (about half the workgroups of equal parts), counted until they
+    # reach 9/16 of the slots (432 at d = 128), at most 12
+    assert n(1, 1, 8192, 128, BF16, 1) == 12   # 374 workgroups at 12 (u = 6: 24 key tiles per part)
+    assert n(1, 2, 8192, 128, BF16, 1) == 6    # 2 x 219 = 438
+    assert n(1, 4, 8192, 128, BF16, 1) == 3    # 4 x 126 = 504 (4 x 96 = 384 at 2)
+    assert n(1, 8, 4096, 128, BF16, 1) == 3    # 256 query tiles: still proportional
+    assert n(1, 8, 8192, 128, BF16, 1) == 2    # 512 query tiles: equal parts, as without the mask
+    assert n(2, 32, 8192, 128, BF16, 1) == 1
+    assert n(1, 1, 64, 128, BF16, 1) == 1      # two key tiles: no split
     # fp32 inputs (64-key tiles on the fp32 MFMA) split down to one tile per part
-    assert capi.fa_splitkv_num_splits(1, 1, 256, 64, capi.FA_DTYPE_F32) == 4
-    assert capi.fa_splitkv_num_splits(1, 1, 64, 64, capi.FA_DTYPE_F32) == 1
-    assert capi.fa_splitkv_num_splits(1, 1, 0, 128, BF16) == capi.FA_ERR_SHAPE
-    assert capi.fa_splitkv_num_splits(1, 1, 64, 80, BF16) == capi.FA_ERR_HEADDIM
-    assert capi.fa_splitkv_num_splits(1, 1, 64, 64, 9) == capi.FA_ERR_DTYPE
+    assert n(1, 1, 256, 64, capi.FA_DTYPE_F32, 0) == 4
+    assert n(1, 1, 256, 64, capi.FA_DTYPE_F32, 1) == 4
+    assert n(1, 1, 64, 64, capi.FA_DTYPE_F32, 0) == 1
+    assert n(1, 1, 0, 128, BF16, 0) == capi.FA_ERR_SHAPE
+    assert n(1, 1, 64, 80, BF16, 1) == capi.FA_ERR_HEADDIM
+    assert n(1, 1, 64, 64, 9, 0) == capi.FA_ERR_DTYPE
 
 
 def _split(**kw):

@@ -87,7 +87,7 @@ def test_auto_split_count_on_a_small_grid():
     """One batch, two heads, N=4096: 64 workgroups unsplit, so the library's
     choice splits; the result meets the bar on sampled rows."""
     w = C[C3].with_shape(B=1, H=2, N=4096)
-    s = capi.fa_splitkv_num_splits(w.B, w.H, w.N, w.d, capi.FA_DTYPE_BF16)
+    s = capi.fa_splitkv_num_splits(w.B, w.H, w.N, w.d, capi.FA_DTYPE_BF16, w.causal)
     U.log(f"case auto split: B,H,N,d={w.B},{w.H},{w.N},{w.d} -> {s} parts")
     assert s > 1
     x = W.generate(w)

@@ -132,3 +132,92 @@ def test_schedule_is_a_bijection_in_heavy_first_order(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert " 0 bad" in r.stdout
+
+
+PARTS_DRIVER = r"""
+#include <cstdio>
+#include <vector>
+#include "work_item.h"
+
+// Causal split-KV parts: query tile qt of n_q (block_r rows) sees the key
+// tiles of its causal extent; the parts of a launch whose longest tile gets
+// at most S parts.
+int main() {
+    long cases = 0, bad = 0;
+    const int shapes[][2] = {{128, 32}, {256, 64}, {128, 64}};  // block_r, block_c
+    const int Ns[] = {1, 31, 32, 127, 128, 129, 200, 1000, 2048, 4095, 8192, 8193, 32768};
+    const int Ss[] = {1, 2, 3, 4, 5, 7, 8, 12, 16, 24, 64};
+    const int heads[] = {1, 2, 3, 8, 16};
+    for (auto& sh : shapes)
+        for (int N : Ns)
+            for (int S : Ss) {
+                const int BR = sh[0], BC = sh[1], r = BR / BC;
+                const int n_q = (N + BR - 1) / BR, n_k = (N + BC - 1) / BC;
+                const int u = fa::split_unit(n_k, r, S);
+                const int s_last = (n_k + u * r - 1) / (u * r);
+                const long long P = fa::parts_per_head(n_q, u, s_last);
+                bool ok = u >= 1 && s_last >= 1 && s_last <= S;
+                long long sum = 0;
+                for (int qt = 0; qt < n_q && ok; ++qt) {
+                    const int np = fa::parts_of(qt, n_q, u, s_last);
+                    if (fa::parts_before(qt, u) != sum && qt < n_q) { printf("parts_before qt=%d\n", qt); ok = false; }
+                    sum += np;
+                    // every part of the causal extent holds at most u*r key tiles
+                    const int ext = (qt == n_q - 1 ? N : (qt + 1) * BR);
+                    const int nt = (ext + BC - 1) / BC;
+                    const int per = (nt + np - 1) / np;
+                    if (np < 1 || np > s_last || per > u * r) { printf("parts BR=%d BC=%d N=%d S=%d qt=%d np=%d per=%d\n", BR, BC, N, S, qt, np, per); ok = false; }
+                }
+                if (ok && sum != P) { printf("P BR=%d N=%d S=%d\n", BR, N, S); ok = false; }
+                // the longest tile's part length is what S asks for, no coarser
+                if (ok && n_k >= S && u * r > r * (((n_k + S - 1) / S + r - 1) / r)) { printf("u too large\n"); ok = false; }
+                for (int H : heads) {
+                    if (!ok) break;
+                    const long long grid = (long long)H * P;
+                    const int mode = fa::xcd_mode_for(H, grid);
+                    std::vector<int> seen((size_t)H * n_q * S, 0);
+                    std::vector<int> prev_qt((size_t)H, n_q);
+                    for (long long b = 0; b < grid && ok; ++b) {
+                        int bh = -1, qt = -1, s = -1;
+                        long long k = -1;
+                        fa::schedule_parts((int)b, (int)grid, P, mode, &bh, &k);
+                        if (bh < 0 || bh >= H || k < 0 || k >= P) { printf("range b=%lld\n", b); ok = false; break; }
+                        fa::locate_part(k, n_q, u, s_last, &qt, &s);
+                        if (qt < 0 || qt >= n_q || s < 0 || s >= fa::parts_of(qt, n_q, u, s_last)) { printf("locate k=%lld\n", k); ok = false; break; }
+                        ++seen[((size_t)bh * n_q + qt) * S + s];
+                        if (mode == fa::kXcdHeads && bh % 8 != (int)(b % 8)) { printf("head %d on XCD %lld\n", bh, b % 8); ok = false; }
+                        // each head's parts run from the last query tile to the first
+                        if (mode != fa::kXcdChunks) {
+                            if (qt > prev_qt[(size_t)bh]) { printf("order H=%d N=%d S=%d\n", H, N, S); ok = false; }
+                            prev_qt[(size_t)bh] = qt;
+                        }
+                    }
+                    long long used = 0;
+                    for (size_t i = 0; i < seen.size() && ok; ++i) {
+                        if (seen[i] > 1) { printf("part twice H=%d N=%d S=%d\n", H, N, S); ok = false; }
+                        used += seen[i];
+                    }
+                    if (ok && used != grid) { printf("not every part H=%d N=%d S=%d\n", H, N, S); ok = false; }
+                    ++cases;
+                }
+                if (!ok) ++bad;
+            }
+    printf("%ld cases, %ld bad\n", cases, bad);
+    return bad != 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not found")
+def test_causal_split_parts_cover_every_part_once(tmp_path):
+    """Causal split-KV launches: every (head, query tile, part) with part <
+    parts_of(tile) is one workgroup, no part holds more than u*r key tiles of
+    its tile's causal extent, the longest tile has at most the requested
+    count, and each head's parts run from the last query tile to the first."""
+    src = tmp_path / "parts.cpp"
+    src.write_text(PARTS_DRIVER)
+    exe = tmp_path / "parts"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", CSRC, str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr
+    assert " 0 bad" in r.stdout
