@@ -43,20 +43,46 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
     const int S = mp.split_u > 0
                       ? parts_of((int)(row % mp.N) / mp.block_r, mp.n_qtiles, mp.split_u, mp.n_splits)
                       : mp.n_splits;
+    // Parts in groups of kGroup whose loads are all issued before the first
+    // is used, instead of a loop that waits for each part's load in turn (at
+    // B*H = 1, N = 8192, about 6 parts per row: 9.3 -> 7.0 us; groups of 8
+    // took more registers and were slower with 2 parts per row); the
+    // additions keep the order s = 0, 1, ..., S - 1.
+    constexpr int kGroup = 4;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, mp.ws_lse[(long long)s * mp.rows + row]);
+    for (int s0 = 0; s0 < S; s0 += kGroup) {
+        float l[kGroup];
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i)
+            l[i] = s0 + i < S ? mp.ws_lse[(long long)(s0 + i) * mp.rows + row] : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) M = fmaxf(M, l[i]);
+    }
     float o[4] = {0.f, 0.f, 0.f, 0.f};
     float out_lse = -INFINITY;
     float inv = 0.f;
     if (M != -INFINITY) {
         float L = 0.f;
-        for (int s = 0; s < S; ++s) {
-            const long long pr = (long long)s * mp.rows + row;
-            const float w = __builtin_amdgcn_exp2f((mp.ws_lse[pr] - M) * kLog2e);  // e^(LSE_s - M)
-            const f32x4 x = *reinterpret_cast<const f32x4*>(mp.ws_o + pr * D + 4 * t);
-            L += w;
+        for (int s0 = 0; s0 < S; s0 += kGroup) {
+            float l[kGroup];
+            f32x4 x[kGroup];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = __builtin_fmaf(w, x[i], o[i]);
+            for (int i = 0; i < kGroup; ++i) {
+                const long long pr = (long long)(s0 + i) * mp.rows + row;
+                if (s0 + i < S) {
+                    l[i] = mp.ws_lse[pr];
+                    x[i] = *reinterpret_cast<const f32x4*>(mp.ws_o + pr * D + 4 * t);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                if (s0 + i < S) {
+                    const float w = __builtin_amdgcn_exp2f((l[i] - M) * kLog2e);  // e^(LSE_s - M)
+                    L += w;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = __builtin_fmaf(w, x[i][j], o[j]);
+                }
+            }
         }
         inv = 1.f / L;
         out_lse = M + __builtin_amdgcn_logf(L) / kLog2e;  // ln L = log2 L / log2 e
