@@ -160,19 +160,19 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 }
 
 // Four consecutive values of an output row, times `inv`, in the output type
-// (16 bytes for fp32, 8 for bf16/fp16, rounded to nearest even). NT marks the
-// store non-temporal (the `nt` hint): a final output that the launch does not
-// read back, written in one burst as the workgroups finish.
-template <typename T, bool NT = false>
+// (16 bytes for fp32, 8 for bf16/fp16, rounded to nearest even). Plain
+// stores: the non-temporal hint (`nt`) on these per-lane pieces of 32 rows
+// was measured at 4.4x the algorithmic HBM write bytes on the headline
+// workload (575 against 130 MiB per launch; 1.7x for fp32 O at d = 64),
+// where the L2 otherwise merges them into whole lines.
+template <typename T>
 __device__ __forceinline__ void store_row4(char* dst, const float* v4, float inv) {
     if constexpr (std::is_same_v<T, F32>) {
         const f32x4 r = {v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv};
-        if constexpr (NT) __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(dst));
-        else *reinterpret_cast<f32x4*>(dst) = r;
+        *reinterpret_cast<f32x4*>(dst) = r;
     } else {
         const u32x2 r = {pack2<T>(v4[0] * inv, v4[1] * inv), pack2<T>(v4[2] * inv, v4[3] * inv)};
-        if constexpr (NT) __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(dst));
-        else *reinterpret_cast<u32x2*>(dst) = r;
+        *reinterpret_cast<u32x2*>(dst) = r;
     }
 }
 

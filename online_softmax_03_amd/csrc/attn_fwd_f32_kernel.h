@@ -260,7 +260,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(Params p) {
                 const int d0 = 32 * db + 8 * g + 4 * hh;
                 const float v4[4] = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2],
                                      acc[db][4 * g + 3]};
-                store_row4<F32, true>(orow + d0 * 4, v4, inv);
+                store_row4<F32>(orow + d0 * 4, v4, inv);
             }
         if (hh == 0) p.lse[(size_t)bh * N + qq] = lse;
     }

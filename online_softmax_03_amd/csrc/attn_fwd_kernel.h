@@ -423,7 +423,7 @@ void attn_fwd_kernel(Params p) {
                 const int d0 = 32 * db + 8 * g + 4 * hh;
                 const float v4[4] = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2],
                                      acc[db][4 * g + 3]};
-                store_row4<TO, true>(orow + d0 * TO::kBytes, v4, inv);
+                store_row4<TO>(orow + d0 * TO::kBytes, v4, inv);
             }
         if (hh == 0) p.lse[(size_t)bh * N + qq] = lse;
     }

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams mp) {
         out_lse = M + __builtin_amdgcn_logf(L) / kLog2e;  // ln L = log2 L / log2 e
     }
     char* orow = reinterpret_cast<char*>(mp.o) + (row * D + 4 * t) * TO::kBytes;
-    store_row4<TO, true>(orow, o, inv);
+    store_row4<TO>(orow, o, inv);
     if (t == 0) mp.lse[row] = out_lse;
 }
 
