@@ -123,3 +123,24 @@ def test_workspace_too_small_is_rejected_before_launch():
     with pytest.raises(A.FaError) as e:
         A.attention_fwd(q, k, v, causal=True, num_splits=2, workspace=ws)
     assert e.value.status == capi.FA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("shape,d,dtype", [((1, 1, 32768), 128, "bf16"), ((1, 2, 8191), 64, "f16")])
+def test_proportional_parts_long_causal(shape, d, dtype):
+    """Causal launches with at most 256 query tiles split each tile's keys
+    in proportion to its causal extent (256 query tiles of 128 rows at
+    N = 32768; a ragged last tile at N = 8191, d = 64): sampled rows against
+    the oracle, every row against fa_fwd."""
+    B, H, N = shape
+    w = C[C3].with_shape(B=B, H=H, N=N, d=d, in_dtype=dtype, out_dtype=dtype, causal=True)
+    s = capi.fa_splitkv_num_splits(B, H, N, d, U.A._DT[W.DTYPES[dtype]], True)
+    U.log(f"case proportional split: B,H,N,d={B},{H},{N},{d} {dtype} -> {s} parts")
+    assert s > 1
+    x = W.generate(w)
+    rows = U.sample_rows(B, H, N, 96, seed=17, causal=True)
+    O, L, _ = U.check_sampled(x, rows, what=f"proportional split N={N} d={d}", num_splits=0)
+    O1, L1 = U.run_gpu(x)
+    dO = float(np.abs(O - O1).max())
+    dL = float(np.abs(L - L1).max())
+    U.log(f"  split vs single pass: max|dO|={dO:.2e} max|dLSE|={dL:.2e}")
+    assert dO <= U.O_TOL[dtype] and dL <= U.LSE_TOL
