@@ -6,13 +6,15 @@
 A step is one attention forward (one fa_fwd call) over the whole workload,
 inputs already resident in HBM. Prints ONE JSON line. The default workload is
 bf16, causal, d=128, N=8192, B=2, H=32. Before the W warm-up steps the step
-runs back to back for --settle-ms (300 ms) so that the GPU has left its idle
-clock, which it takes a few hundred milliseconds of load to do (the first
-ten launches after idle average 1.5 ms, the sustained rate is 1.05 ms); the
-JSON line reports that phase as `settle`, and as `clock` the kernel's clock
-from the committed rocprofv3 counters of this kernel and shape
-(GRBM_GUI_ACTIVE cycles over kernel time) next to the SMU's own reading when
-its metrics table (refreshed about once a second) updated during the run.
+runs back to back for at least --settle-ms (300 ms) so that the GPU has left
+its idle clock, which it takes a few hundred milliseconds of load to do (the
+first ten launches after idle average 1.5 ms, the sustained rate is 1.05
+ms), and on (at most 3 s) until the SMU's metrics table, refreshed about once
+a second, has been read under load; the JSON line reports that phase as
+`settle`, and as `clock` the kernel's clock from the committed rocprofv3
+counters of this kernel and shape (GRBM_GUI_ACTIVE cycles over kernel time)
+next to the SMU's readings of the shader clock and the socket power (with
+the power cap) from the settle phase and the timed steps.
 
 --bwd times the backward (one fa_bwd call per step: the D/LSE pass, the
 dK/dV kernel and the dQ kernel) on the forward's output, with nominal
@@ -164,6 +166,8 @@ class ClockSampler:
     def __init__(self, period_s=0.005):
         self.period_s = period_s
         self.samples = []
+        self.watts = []
+        self.power_cap_w = None
         self.active = False
         self.source = None
         self._stop = False
@@ -184,9 +188,18 @@ class ClockSampler:
 
             def read():
                 m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
-                return m["system_clock_counter"], float(m["current_gfxclk"])
+                try:
+                    w = float(amdsmi.amdsmi_get_power_info(handle)["current_socket_power"])
+                except Exception:
+                    w = None
+                return m["system_clock_counter"], float(m["current_gfxclk"]), w
             read()
-            self.source = "amdsmi gpu_metrics current_gfxclk"
+            try:
+                cap = float(amdsmi.amdsmi_get_power_cap_info(handle)["power_cap"]) / 1e6
+            except Exception:
+                cap = None
+            self.power_cap_w = cap
+            self.source = "amdsmi gpu_metrics current_gfxclk, power_info current_socket_power"
             return read
         except Exception:
             return None
@@ -197,15 +210,20 @@ class ClockSampler:
         while not self._stop:
             if self.active:
                 try:
-                    stamp, mhz = self._read()
+                    stamp, mhz, watts = self._read()
                     if stamp != last:
                         refreshes += 1
                         if refreshes >= 2:
                             self.samples.append(mhz)
+                            if watts is not None:
+                                self.watts.append(watts)
                         last = stamp
                 except Exception:
                     pass
             time.sleep(self.period_s)
+
+    def available(self):
+        return self._read is not None
 
     def close(self):
         self._stop = True
@@ -215,7 +233,9 @@ class ClockSampler:
     def report(self):
         if not self.samples:
             return None
-        return {"median_mhz": _median(self.samples), "samples": len(self.samples), "source": self.source}
+        return {"median_mhz": _median(self.samples),
+                "median_socket_w": _median(self.watts) if self.watts else None,
+                "power_cap_w": self.power_cap_w, "samples": len(self.samples), "source": self.source}
 
 
 def clock_report(sampler, workload, kernel, tile):
@@ -231,12 +251,17 @@ def clock_report(sampler, workload, kernel, tile):
             "smu": sampler.report()}
 
 
-def settle(step, settle_ms):
+def settle(step, settle_ms, clock=None, max_ms=3000.0):
     """Runs `step` back to back for `settle_ms` of wall time (at least once),
-    then synchronises; returns the number of steps run. After idle the GPU
-    starts its clock at a few hundred MHz and takes a few hundred
-    milliseconds of load to reach its working clock; the first ten 1 ms
-    launches of the default workload average 1.5 ms, the next ones 1.05."""
+    and on until `clock` (a ClockSampler) holds a reading of the SMU's
+    metrics table, at most `max_ms` in all; then synchronises and returns the
+    number of steps run and the milliseconds they took. After idle the GPU starts its clock at a few
+    hundred MHz and takes a few hundred milliseconds of load to reach its
+    working clock (the first ten 1 ms launches of the default workload
+    average 1.5 ms, the next ones 1.05); the table refreshes about once a
+    second, and its first refresh under load still averages the idle time
+    before, so a reading of the loaded clock and power takes one to two
+    seconds of this phase."""
     import torch
     n = 0
     t0 = time.perf_counter()
@@ -245,10 +270,12 @@ def settle(step, settle_ms):
         n += 1
         if n % 8 == 0:
             torch.cuda.synchronize()
-            if (time.perf_counter() - t0) * 1e3 >= settle_ms:
+            ms = (time.perf_counter() - t0) * 1e3
+            waiting = clock is not None and clock.available() and not clock.samples
+            if ms >= max_ms or (ms >= settle_ms and not waiting):
                 break
     torch.cuda.synchronize()
-    return n
+    return n, round((time.perf_counter() - t0) * 1e3, 1)
 
 
 def timed_steps(step, stream, steps, warmup, clock=None):
@@ -365,7 +392,7 @@ def bench_softmax(args):
 
     clock = ClockSampler()
     clock.active = True
-    settled = settle(step, args.settle_ms) if args.settle_ms > 0 else 0
+    settled, settled_ms = settle(step, args.settle_ms, clock) if args.settle_ms > 0 else (0, 0.0)
     wall, avg_ms = timed_steps(step, stream, args.steps, args.warmup, clock)
     clock.close()
     launch_ms = per_launch(step, stream, args.steps)
@@ -403,7 +430,7 @@ def bench_softmax(args):
                      "avg_launch_ms": round(avg_s * 1e3, 4),
                      "min_launch_ms": round(min(launch_ms), 4)},
         "clock": clock_report(clock, w.name, kernel, None),
-        "settle": {"ms": args.settle_ms, "steps": settled},
+        "settle": {"ms": settled_ms, "min_ms": args.settle_ms, "steps": settled},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = softmax_cpu_baseline(w, x, args.cpu_seconds)
@@ -487,7 +514,7 @@ def main():
     # clock sampled alongside
     clock = ClockSampler()
     clock.active = True
-    settled = settle(step, args.settle_ms) if args.settle_ms > 0 else 0
+    settled, settled_ms = settle(step, args.settle_ms, clock) if args.settle_ms > 0 else (0, 0.0)
     wall, avg_ms = timed_steps(step, stream, args.steps, args.warmup, clock)
     clock.close()
     launch_ms = per_launch(step, stream, args.steps)
@@ -550,7 +577,7 @@ def main():
                          "flushed_min_launch_ms": round(min(flushed), 4)} if flushed else {})},
         "clock": clock_report(clock, w.name, kernel, None if fp8 else tile) if (splits is None and not args.bwd)
         else {"smu": clock.report()},
-        "settle": {"ms": args.settle_ms, "steps": settled},
+        "settle": {"ms": settled_ms, "min_ms": args.settle_ms, "steps": settled},
     }
     if not args.no_cpu_baseline and not args.bwd:
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

@@ -47,9 +47,13 @@ def test_one_json_line_with_roofline_and_cpu_baseline():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0 and cb["cores"] >= 1
     assert "rows of bf16_causal_n8192_d128" in cb["sample"]
-    assert d["settle"]["steps"] >= 1
+    assert d["settle"]["steps"] >= 1 and d["settle"]["ms"] <= 3500
     assert d["clock"]["counter_ghz"] is None or 0.5 <= d["clock"]["counter_ghz"] <= 2.5
-    assert d["clock"]["smu"] is None or 100 <= d["clock"]["smu"]["median_mhz"] <= 2500
+    smu = d["clock"]["smu"]
+    if smu is not None:  # read under load: the settle phase runs until the SMU table refreshed twice
+        assert 100 <= smu["median_mhz"] <= 2500
+        assert smu["median_socket_w"] is None or 100 <= smu["median_socket_w"] <= 2000
+        assert smu["power_cap_w"] is None or smu["power_cap_w"] > 0
 
 
 @pytest.mark.gpu
