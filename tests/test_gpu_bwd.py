@@ -183,7 +183,7 @@ def _draw(i):
                 seed=51000 + i)
 
 
-RANDOM = [_draw(i) for i in range(40)]
+RANDOM = [_draw(i) for i in range(100)]
 
 
 @pytest.mark.parametrize("i", range(len(RANDOM)))

@@ -191,7 +191,7 @@ def _draw(i):
                 mask=["none", "padding", "general"][int(r.integers(3))], seed=61000 + i)
 
 
-RANDOM = [_draw(i) for i in range(30)]
+RANDOM = [_draw(i) for i in range(60)]
 
 
 @pytest.mark.parametrize("i", range(len(RANDOM)))

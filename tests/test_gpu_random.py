@@ -47,7 +47,7 @@ def _draw(i):
                 route=route, pick=int(r.integers(1 << 30)), seed=41000 + i)
 
 
-DRAWS = [_draw(i) for i in range(200)]
+DRAWS = [_draw(i) for i in range(400)]
 
 
 @pytest.mark.parametrize("i", range(len(DRAWS)))

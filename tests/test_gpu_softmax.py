@@ -176,7 +176,7 @@ def _draw_softmax(i):
                 dist=("uniform", lo, lo + float(r.uniform(0.1, 60.0))), seed=16000 + i)
 
 
-SOFTMAX_RANDOM = [_draw_softmax(i) for i in range(120)]
+SOFTMAX_RANDOM = [_draw_softmax(i) for i in range(200)]
 
 
 @pytest.mark.parametrize("i", range(len(SOFTMAX_RANDOM)))
