@@ -125,11 +125,13 @@ def test_workspace_too_small_is_rejected_before_launch():
     assert e.value.status == capi.FA_ERR_WORKSPACE
 
 
-@pytest.mark.parametrize("shape,d,dtype", [((1, 1, 32768), 128, "bf16"), ((1, 2, 8191), 64, "f16")])
+@pytest.mark.parametrize("shape,d,dtype", [((1, 1, 32768), 128, "bf16"), ((1, 1, 32769), 128, "bf16"),
+                                           ((1, 2, 8191), 64, "f16")])
 def test_proportional_parts_long_causal(shape, d, dtype):
     """Causal launches with at most 256 query tiles split each tile's keys
     in proportion to its causal extent (256 query tiles of 128 rows at
-    N = 32768; a ragged last tile at N = 8191, d = 64): sampled rows against
+    N = 32768; a ragged last tile at N = 8191, d = 64); one more query tile
+    (N = 32769, 257 tiles) takes equal parts again: sampled rows against
     the oracle, every row against fa_fwd."""
     B, H, N = shape
     w = C[C3].with_shape(B=B, H=H, N=N, d=d, in_dtype=dtype, out_dtype=dtype, causal=True)
