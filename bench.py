@@ -157,11 +157,12 @@ def traffic(workload, kernel=KERNEL_PREFIX, tile=None):
 
 class ClockSampler:
     """Reads the GPU's shader clock from the SMU metrics table through amdsmi
-    (current_gfxclk, MHz) in a background thread while `active`. The table
-    is refreshed about once a second and its clock is an average over the
-    period before the refresh, so the first refresh after the sampler
-    starts still covers time before the load: only the readings of later
-    refreshes count, and a run shorter than two refresh periods gets none."""
+    (current_gfxclk, MHz), with the socket power (W) and the power cap, in a
+    background thread while `active`. The table is refreshed about once a
+    second and its clock is an average over the period before the refresh,
+    so the first refresh after the sampler starts still covers time before
+    the load: only the readings of later refreshes count, and a run shorter
+    than two refresh periods gets none."""
 
     def __init__(self, period_s=0.005):
         self.period_s = period_s
@@ -241,8 +242,8 @@ class ClockSampler:
 def clock_report(sampler, workload, kernel, tile):
     """The clock the kernel runs at: GRBM_GUI_ACTIVE cycles over kernel time
     from the committed rocprofv3 counter summary of this kernel, workload and
-    tile (when taken on the current sources), and the SMU's reading when its
-    metrics table refreshed during the run."""
+    tile (when taken on the current sources), and the SMU's clock and power
+    readings under the run's load (ClockSampler)."""
     from online_softmax_03_amd import profiling
     c = profiling.current_counters(workload, kernel, tile)
     return {"counter_ghz": None if c is None else round(c["clock_ghz"], 3),
@@ -255,9 +256,9 @@ def settle(step, settle_ms, clock=None, max_ms=3000.0):
     """Runs `step` back to back for `settle_ms` of wall time (at least once),
     and on until `clock` (a ClockSampler) holds a reading of the SMU's
     metrics table, at most `max_ms` in all; then synchronises and returns the
-    number of steps run and the milliseconds they took. After idle the GPU starts its clock at a few
-    hundred MHz and takes a few hundred milliseconds of load to reach its
-    working clock (the first ten 1 ms launches of the default workload
+    number of steps run and the milliseconds they took. After idle the GPU
+    starts its clock at a few hundred MHz and takes a few hundred
+    milliseconds of load to reach its working clock (the first ten 1 ms launches of the default workload
     average 1.5 ms, the next ones 1.05); the table refreshes about once a
     second, and its first refresh under load still averages the idle time
     before, so a reading of the loaded clock and power takes one to two
