@@ -472,7 +472,7 @@ def main():
     if fp8:
         tile = (128, 64)  # the FP8 kernel's one shape: 4 waves x 32 queries, 64-key tiles
     elif tile is None:
-        st, tile = capi.fa_default_tile(w.N, w.d, A._DT[q.dtype], A._DT[out_dt], int(w.causal),
+        st, tile = capi.fa_default_tile(w.B, w.H, w.N, w.d, A._DT[q.dtype], A._DT[out_dt], int(w.causal),
                                         int(mask is not None))
         assert st == 0
 

@@ -109,17 +109,25 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const uint8_t* key_padding_mask, fa_dtype_t in_dtype, fa_dtype_t out_dtype,
            hipStream_t stream);
 
-/* fa_fwd_ex — fa_fwd with an explicit tile shape (NULL = default). Returns
- * FA_ERR_TILE if no kernel exists for that shape with these arguments. */
+/* fa_fwd_ex — fa_fwd with an explicit tile shape. NULL or {0, 0} is the
+ * library's choice for the shape (fa_default_tile); a zero in one field takes
+ * that field from the base tile (128 x 32 for 16-bit d = 128, 256 x 64 for
+ * 16-bit d = 64, 128 x 64 for fp32). Returns FA_ERR_TILE if no kernel exists
+ * for that shape with these arguments. */
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, float scale, int causal,
               const uint8_t* key_padding_mask, fa_dtype_t in_dtype, fa_dtype_t out_dtype,
               hipStream_t stream, const fa_tile* tile);
 
-/* fa_default_tile — the tile shape fa_fwd would use for these arguments.
- * Writes *out and returns FA_OK, or returns a negative fa_status. Host only. */
-int fa_default_tile(int N, int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype, int causal,
-                    int has_mask, fa_tile* out);
+/* fa_default_tile — the tile shape fa_fwd would use for these arguments:
+ * for 16-bit inputs at d = 128, 256 x 64 when every workgroup has a long key
+ * loop and the grid of 256-row tiles, G = B*H*ceil(N/256), still covers the
+ * CUs (causal: N >= 8192, G >= 384 and, below N = 16384, G <= 1024;
+ * non-causal: N >= 4096 and G >= 256), else the base tile. Writes *out and returns FA_OK, or returns a negative fa_status
+ * (FA_ERR_NULL, FA_ERR_SHAPE for B, H or N <= 0, FA_ERR_HEADDIM,
+ * FA_ERR_DTYPE). Host only, no HIP call. */
+int fa_default_tile(int B, int H, int N, int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype,
+                    int causal, int has_mask, fa_tile* out);
 
 /* fa_tile_supported — FA_OK if fa_fwd_ex accepts `tile` for (d, in_dtype,
  * out_dtype), FA_ERR_TILE otherwise. Host only, no HIP call. */

@@ -67,7 +67,7 @@ def library():
             lib.fa_fwd_ex.restype = _I
             lib.fa_fwd_ex.argtypes = _FWD_ARGS + [ctypes.POINTER(fa_tile)]
             lib.fa_default_tile.restype = _I
-            lib.fa_default_tile.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.POINTER(fa_tile)]
+            lib.fa_default_tile.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(fa_tile)]
             lib.fa_tile_supported.restype = _I
             lib.fa_tile_supported.argtypes = [_I, _I, _I, ctypes.POINTER(fa_tile)]
             lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
@@ -110,10 +110,10 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask, in_d
                                in_dtype, out_dtype, stream, t)
 
 
-def fa_default_tile(N, d, in_dtype, out_dtype, causal, has_mask):
+def fa_default_tile(B, H, N, d, in_dtype, out_dtype, causal, has_mask):
     """Returns (status, (block_r, block_c))."""
     t = fa_tile()
-    st = library().fa_default_tile(N, d, in_dtype, out_dtype, causal, has_mask, ctypes.byref(t))
+    st = library().fa_default_tile(B, H, N, d, in_dtype, out_dtype, causal, has_mask, ctypes.byref(t))
     return st, (t.block_r, t.block_c)
 
 

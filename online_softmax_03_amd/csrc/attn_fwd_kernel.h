@@ -54,18 +54,20 @@ namespace fa {
 
 // ---------------------------------------------------------------- kernel
 
-// Waves per SIMD the split-KV forms are held to: the host sizes its split
+// Waves per SIMD the 128 x 32 tile at d = 128 is held to in its split-KV and
+// key-masked forms: three (at most 168 registers). The host sizes its split
 // count by the workgroups a compute unit holds (resident_wgs_per_cu in
-// fa_api.hip), three for the 128 x 32 tile at d = 128 (at most 168
-// registers). The 256 x 64 tile at d = 64 meets its count of two (at most 128
-// registers) by itself. The other forms carry no bound.
-template <int D, int BC, int NW, bool SPLIT>
+// fa_api.hip), and the masked forms would otherwise take 2-3 registers more
+// than three waves allow. Its other forms stay well below the bound without
+// it (and were 0.3% slower with it on the causal bf16 workload); the 256 x 64
+// tile at d = 64 meets its count of two (at most 128 registers) by itself.
+template <int D, int BC, int NW, bool SPLIT, bool MASK>
 constexpr int min_waves_per_eu() {
-    return (SPLIT && D == 128 && BC == 32 && NW == 4) ? 3 : 1;
+    return (D == 128 && BC == 32 && NW == 4 && (SPLIT || MASK)) ? 3 : 1;
 }
 
 template <int D, int BC, int NW, typename TI, typename TO, bool CAUSAL, bool MASK, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<D, BC, NW, SPLIT>())))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<D, BC, NW, SPLIT, MASK>())))
 void attn_fwd_kernel(Params p) {
     // The body uses device-only types (buffer resources), so the host pass,
     // which only needs the launch stub, does not see it.
@@ -205,8 +207,14 @@ void attn_fwd_kernel(Params p) {
     const bool wave_live = qw0 < N;
     const int qq = qw0 + col;  // this lane's query
 
-    // K operand rows are 32*kb + col: one chunk XOR per lane.
+    // K operand rows are 32*kb + col: one chunk XOR per lane. The per-lane
+    // offsets within a tile are computed once, like the V^T ones below, so
+    // that both buffers read through the same registers with the buffer and
+    // the key block in the instruction's constant offset.
     const int sw_col = swz<CH>(col);
+    u32 k_off[NDC];
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) k_off[dc] = (u32)(col * ROWB + (((2 * dc + hh) ^ sw_col) << 4));
     // V^T transpose reads (16-bit path): within each 16-lane group, lane
     // 4r + c addresses tile row key0 + r at d offset dbase + 4c, where key0 =
     // 32kb + 16t + 8*half + 4*hh and dbase = 32db + 16*(group & 1). The XOR
@@ -242,9 +250,7 @@ void attn_fwd_kernel(Params p) {
         for (int dc = 0; dc < NDC; ++dc) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const int chunk = (2 * dc + hh) ^ sw_col;
-                const u32x4 a =
-                    *reinterpret_cast<const FA_LDS u32x4*>(kt + (kb * 32 + col) * ROWB + chunk * 16);
+                const u32x4 a = *reinterpret_cast<const FA_LDS u32x4*>(kt + kb * 32 * ROWB + k_off[dc]);
                 s[kb] = mfma32x32x16<TI>(a, qop[dc], s[kb]);
             }
         }

@@ -34,13 +34,33 @@ bool dtype_pair_ok(int in_dtype, int out_dtype) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Defaults from the tile sweep on MI355X (the five study workloads): for
-// 16-bit inputs, d = 128 runs best with 128 query rows and 32-key tiles (lower
-// register use, three waves per SIMD) and d = 64 with 256 query rows and
-// 64-key tiles. fp32 inputs have one tile shape, 128 x 64.
+// Base tiles from the tile sweep on MI355X: for 16-bit inputs, d = 128 with
+// 128 query rows and 32-key tiles (three waves per SIMD; the split-KV forms
+// and the key-masked launches of short sequences use it) and d = 64 with 256
+// query rows and 64-key tiles. fp32 inputs have one tile shape, 128 x 64.
 fa_tile default_tile(int d, int in_dtype) {
     if (in_dtype == FA_DTYPE_F32) return fa_tile{128, 64};
     return d == 128 ? fa_tile{128, 32} : fa_tile{256, 64};
+}
+
+// The tile fa_fwd takes when the caller names none. For 16-bit d = 128,
+// 256 x 64 (eight waves sharing every 64-key tile: half the LDS fills, waits
+// and barriers per MFMA of 128 x 32, at two waves per SIMD) is ahead once each
+// workgroup's key loop is long and its grid still covers the CUs. Same-process
+// A/B on two boxes: causal N = 32768 +2.3-3.5%, N = 16384 (8 heads) +3.5%,
+// N = 8192 with 16 heads +2.9-3.4% and 12 heads +17%, non-causal N = 8192
+// +5-10%, N = 4096 +2%. Behind with short loops (causal N <= 6144: -0.1 to
+// -2.4%, non-causal N = 2048: -0.7%) and with 256 or fewer causal workgroups
+// (-4.9 to -5.9%). Causal N = 8192 over 2048 workgroups (2 x 32 heads) is a
+// tie: +0.6-1.8% in same-process runs, -1.4% over three bench runs of each,
+// so the base tile keeps it.
+fa_tile auto_tile(int B, int H, int N, int d, int in_dtype, int causal) {
+    const fa_tile t = default_tile(d, in_dtype);
+    if (in_dtype == FA_DTYPE_F32 || d != 128) return t;
+    const long long wide_grid = (long long)B * H * ((N + 255) / 256);
+    const bool wide = causal ? (N >= 8192 && wide_grid >= 384 && (N >= 16384 || wide_grid <= 1024))
+                             : (N >= 4096 && wide_grid >= 256);
+    return wide ? fa_tile{256, 64} : t;
 }
 
 // The split-KV kernels write fp32 partials whatever the final output dtype,
@@ -69,9 +89,10 @@ const fa::MergeEntry* find_merge(int d, int out_dtype) {
 
 // Workgroups of the default-tile split-KV kernel that one compute unit holds
 // at once (its register use): 3 for the 16-bit d = 128 tile (4 waves of at
-// most 168 VGPRs, a bound its split forms carry), 2 for the 16-bit d = 64 tile
-// (8 waves of at most 128) and for the fp32 d = 64 tile (4 waves of at most
-// 256), 1 for the fp32 d = 128 tile (4 waves of 256 VGPRs plus AGPRs).
+// most 168 VGPRs, a bound its split and key-masked forms carry), 2 for the
+// 16-bit d = 64 tile (8 waves of at most 128) and for the fp32 d = 64 tile
+// (4 waves of at most 256), 1 for the fp32 d = 128 tile (4 waves of 256
+// VGPRs plus AGPRs).
 int resident_wgs_per_cu(int d, int in_dtype) {
     if (in_dtype == FA_DTYPE_F32) return d == 128 ? 1 : 2;
     return d == 128 ? 3 : 2;
@@ -154,12 +175,13 @@ void fill_params(fa::Params& prm, const void* q, const void* k, const void* v, v
     prm.ws_lse = nullptr;
 }
 
-fa_tile resolve(int d, int in_dtype, const fa_tile* tile) {
+// The caller's tile: NULL or {0, 0} is the library's choice for the shape;
+// a zero in one field takes that field from the base tile.
+fa_tile resolve(int B, int H, int N, int d, int in_dtype, int causal, const fa_tile* tile) {
+    if (!tile || (tile->block_r == 0 && tile->block_c == 0)) return auto_tile(B, H, N, d, in_dtype, causal);
     fa_tile t = default_tile(d, in_dtype);
-    if (tile) {
-        if (tile->block_r != 0) t.block_r = tile->block_r;
-        if (tile->block_c != 0) t.block_c = tile->block_c;
-    }
+    if (tile->block_r != 0) t.block_r = tile->block_r;
+    if (tile->block_c != 0) t.block_c = tile->block_c;
     return t;
 }
 
@@ -239,19 +261,18 @@ int launch_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 extern "C" {
 
 int fa_tile_supported(int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype, const fa_tile* tile) {
-    const fa_tile t = resolve(d, in_dtype, tile);
+    const fa_tile t = resolve(1, 1, 1, d, in_dtype, 0, tile);  // NULL, {0, 0}: the base tile
     return find(d, t, in_dtype, out_dtype, 0, 0) ? FA_OK : FA_ERR_TILE;
 }
 
-int fa_default_tile(int N, int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype, int causal, int has_mask,
-                    fa_tile* out) {
-    (void)causal;
+int fa_default_tile(int B, int H, int N, int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype, int causal,
+                    int has_mask, fa_tile* out) {
     (void)has_mask;
     if (!out) return FA_ERR_NULL;
-    if (N <= 0) return FA_ERR_SHAPE;
+    if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
     if (!dtype_pair_ok(in_dtype, out_dtype)) return FA_ERR_DTYPE;
-    *out = default_tile(d, in_dtype);
+    *out = auto_tile(B, H, N, d, in_dtype, causal);
     return FA_OK;
 }
 
@@ -260,7 +281,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
               fa_dtype_t out_dtype, hipStream_t stream, const fa_tile* tile) {
     const int st = check_common(q, k, v, o, lse, B, H, N, d, scale, in_dtype, out_dtype);
     if (st != FA_OK) return st;
-    const fa_tile t = resolve(d, in_dtype, tile);
+    const fa_tile t = resolve(B, H, N, d, in_dtype, causal, tile);
     if (t.block_r <= 0 || t.block_r % 32 != 0) return FA_ERR_TILE;
     // Sizes: every byte offset is computed in 64 bits on the device, but a
     // row index times the row size must fit in 32 bits, and so must the grid.

@@ -352,8 +352,9 @@ def _tiles(a) -> None:
     lines += ["", "The clock column divides the counted cycles by the unprofiled launch time, so it is an estimate "
               "of the clock the kernel ran at. VGPRs allocated = rocprofv3's VGPR_Count x 2: rocprofv3 "
               "multiplies the kernel descriptor's register granules by 4, but gfx950's unified register file "
-              "allocates 8 registers per granule (e.g. the 128 x 32 tile: the compiler's 162 VGPRs round up to "
-              "21 granules = 168 registers, which rocprofv3 prints as 84). SQ_INSTS_VALU counts the MFMA "
+              "allocates 8 registers per granule (e.g. the 128 x 32 tile at d = 128: 152 registers in 19 "
+              "granules, which rocprofv3 prints as 76). Where LDS already limits the workgroups per CU, the "
+              "compiler allocates more registers than the kernel uses. SQ_INSTS_VALU counts the MFMA "
               "instructions too, so VALU / MFMA includes 1 for the MFMA itself."]
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")

@@ -62,12 +62,16 @@ int main(void) {
         EXPECT(fa_fwd_ex(P, P, P, P, L, 1, 1, 8, 64, 0.1f, 0, NULL, BF, BF, s, &t), FA_ERR_TILE);
         EXPECT(fa_tile_supported(128, BF, BF, &t), FA_ERR_TILE);
         EXPECT(fa_tile_supported(128, BF, BF, NULL), FA_ERR_TILE);
-        EXPECT(fa_default_tile(8192, 128, BF, BF, 1, 0, &t), FA_OK);
-        EXPECT(t.block_r > 0 && t.block_c > 0, 1);
-        EXPECT(fa_default_tile(8192, 128, BF, BF, 1, 0, NULL), FA_ERR_NULL);
-        EXPECT(fa_default_tile(0, 128, BF, BF, 1, 0, &t), FA_ERR_SHAPE);
-        EXPECT(fa_default_tile(64, 32, BF, BF, 1, 0, &t), FA_ERR_HEADDIM);
-        EXPECT(fa_default_tile(64, 64, F32, BF, 1, 0, &t), FA_ERR_DTYPE);
+        EXPECT(fa_default_tile(1, 8, 32768, 128, BF, BF, 1, 0, &t), FA_OK);
+        EXPECT(t.block_r == 256 && t.block_c == 64, 1);
+        EXPECT(fa_default_tile(1, 8, 8192, 128, BF, BF, 1, 0, &t), FA_OK);
+        EXPECT(t.block_r == 128 && t.block_c == 32, 1);
+        EXPECT(fa_default_tile(2, 32, 8192, 128, BF, BF, 1, 0, NULL), FA_ERR_NULL);
+        EXPECT(fa_default_tile(1, 1, 0, 128, BF, BF, 1, 0, &t), FA_ERR_SHAPE);
+        EXPECT(fa_default_tile(0, 1, 64, 128, BF, BF, 1, 0, &t), FA_ERR_SHAPE);
+        EXPECT(fa_default_tile(1, -1, 64, 128, BF, BF, 1, 0, &t), FA_ERR_SHAPE);
+        EXPECT(fa_default_tile(1, 1, 64, 32, BF, BF, 1, 0, &t), FA_ERR_HEADDIM);
+        EXPECT(fa_default_tile(1, 1, 64, 64, F32, BF, 1, 0, &t), FA_ERR_DTYPE);
     }
 
     /* split-KV: workspace sizes, the split count over many shapes, the entry */

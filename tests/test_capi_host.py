@@ -79,17 +79,40 @@ def test_fa_fwd_is_fa_fwd_ex_with_default_tile():
 
 
 def test_default_tile_and_supported_tiles():
-    st, t = capi.fa_default_tile(8192, 128, BF16, BF16, 1, 0)
+    st, t = capi.fa_default_tile(2, 32, 8192, 128, BF16, BF16, 1, 0)
     assert st == capi.FA_OK and t[0] % 32 == 0 and t[1] % 32 == 0
     assert capi.fa_tile_supported(128, BF16, BF16, t) == capi.FA_OK
     assert capi.fa_tile_supported(128, BF16, BF16, (0, 0)) == capi.FA_OK
     assert capi.fa_tile_supported(128, BF16, BF16, (96, 64)) == capi.FA_ERR_TILE
-    assert capi.fa_default_tile(8192, 96, BF16, BF16, 1, 0)[0] == capi.FA_ERR_HEADDIM
-    assert capi.fa_default_tile(0, 128, BF16, BF16, 1, 0)[0] == capi.FA_ERR_SHAPE
+    assert capi.fa_default_tile(1, 1, 8192, 96, BF16, BF16, 1, 0)[0] == capi.FA_ERR_HEADDIM
+    assert capi.fa_default_tile(1, 1, 0, 128, BF16, BF16, 1, 0)[0] == capi.FA_ERR_SHAPE
+    assert capi.fa_default_tile(0, 1, 64, 128, BF16, BF16, 1, 0)[0] == capi.FA_ERR_SHAPE
+    assert capi.fa_default_tile(1, 0, 64, 128, BF16, BF16, 1, 0)[0] == capi.FA_ERR_SHAPE
     for d in (64, 128):
         for pair in ((BF16, BF16), (BF16, F32), (F16, F16), (F16, F32), (F32, F32)):
-            st, t = capi.fa_default_tile(4096, d, *pair, 0, 0)
-            assert st == capi.FA_OK and capi.fa_tile_supported(d, *pair, t) == capi.FA_OK
+            for B, H, N, causal in ((1, 1, 4096, 0), (2, 32, 8192, 1), (1, 8, 32768, 1), (4, 16, 2048, 0)):
+                st, t = capi.fa_default_tile(B, H, N, d, *pair, causal, 0)
+                assert st == capi.FA_OK and capi.fa_tile_supported(d, *pair, t) == capi.FA_OK
+
+
+@pytest.mark.parametrize("B,H,N,causal,tile", [
+    # 16-bit d = 128: 256 x 64 for long key loops over a grid that covers the CUs
+    (1, 8, 32768, 1, (256, 64)), (1, 12, 8192, 1, (256, 64)), (1, 16, 8192, 1, (256, 64)),
+    (1, 8, 16384, 1, (256, 64)), (2, 32, 16384, 1, (256, 64)), (4, 16, 4096, 0, (256, 64)),
+    (1, 8, 8192, 0, (256, 64)), (2, 32, 8192, 0, (256, 64)),
+    # short loops, 256 and fewer causal workgroups of 256 rows, or causal
+    # N = 8192 over more than 1024 of them: 128 x 32
+    (2, 32, 8192, 1, (128, 32)), (1, 8, 8192, 1, (128, 32)), (1, 4, 16384, 1, (128, 32)),
+    (2, 32, 6144, 1, (128, 32)), (4, 32, 4096, 1, (128, 32)), (8, 16, 2048, 0, (128, 32)),
+    (1, 4, 8192, 0, (128, 32)), (1, 1, 256, 0, (128, 32)),
+])
+def test_default_tile_follows_the_shape_rule(B, H, N, causal, tile):
+    for dt in (BF16, F16):
+        for has_mask in (0, 1):
+            assert capi.fa_default_tile(B, H, N, 128, dt, dt, causal, has_mask) == (capi.FA_OK, tile)
+    # d = 64 and fp32 inputs keep their one base tile
+    assert capi.fa_default_tile(B, H, N, 64, BF16, BF16, causal, 0) == (capi.FA_OK, (256, 64))
+    assert capi.fa_default_tile(B, H, N, 128, F32, F32, causal, 0) == (capi.FA_OK, (128, 64))
 
 
 def test_splitkv_workspace_bytes():

@@ -205,6 +205,23 @@ def test_nondefault_stream_and_repeat():
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
 
 
+@pytest.mark.parametrize("B,H,N,causal,tile", [(1, 16, 4096, False, (256, 64)), (1, 12, 8192, True, (256, 64)),
+                                              (1, 8, 8192, True, (128, 32))])
+def test_default_tile_is_the_shape_rule(B, H, N, causal, tile):
+    """Without a tile, fa_fwd runs the tile fa_default_tile names for the
+    shape: bit-identical to fa_fwd_ex with that tile, and the oracle agrees
+    on sampled rows."""
+    from online_softmax_03_amd import capi
+    w = C[C3].with_shape(B=B, H=H, N=N, causal=causal)
+    assert capi.fa_default_tile(B, H, N, 128, capi.FA_DTYPE_BF16, capi.FA_DTYPE_BF16, int(causal), 0) == (0, tile)
+    x = W.generate(w)
+    U.log(f"case default tile B,H,N={B},{H},{N} causal={causal} -> {tile}")
+    O1, L1 = U.run_gpu(x)
+    O2, L2 = U.run_gpu(x, tile=tile)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    U.check_sampled(x, U.sample_rows(B, H, N, 48, 5 + N, causal), what=f"default tile {tile}")
+
+
 @pytest.mark.parametrize("d,dtype,causal", [(64, "f16", False), (128, "bf16", True), (64, "bf16", True),
                                             (128, "f16", False)])
 def test_general_key_mask(d, dtype, causal):

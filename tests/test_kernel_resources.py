@@ -9,8 +9,11 @@ note (offload bundle -> gfx950 ELF -> NT_AMDGPU_METADATA, msgpack) and check
 the figures the host logic depends on. No GPU is needed.
 
 gfx950 has a unified register file of 512 registers per lane and SIMD; a
-wave's allocation is its `.vgpr_count` (architectural plus accumulation
-registers) rounded up to 8, so waves per SIMD = 512 // that, at most 8.
+wave's allocation is the register block count of its kernel descriptor
+(compute_pgm_rsrc1 bits 5:0, blocks of 8 registers, architectural and
+accumulation registers together), so waves per SIMD = 512 // that, at most 8.
+The descriptor can allocate more than the metadata's `.vgpr_count` when LDS
+already caps the occupancy (the compiler then widens the register budget).
 """
 import shutil
 import struct
@@ -24,7 +27,9 @@ msgpack = pytest.importorskip("msgpack")
 
 LDS_PER_CU = 160 * 1024
 NT_AMDGPU_METADATA = 32
+SHT_SYMTAB = 2
 SHT_NOTE = 7
+KD_RSRC1 = 48  # byte offset of compute_pgm_rsrc1 in a kernel descriptor
 
 
 def _sections(elf: bytes):
@@ -39,8 +44,28 @@ def _sections(elf: bytes):
     return out
 
 
+def _descriptor_registers(co: bytes):
+    """{kernel symbol: registers its descriptor allocates per lane}."""
+    shoff = struct.unpack_from("<Q", co, 0x28)[0]
+    shnum = struct.unpack_from("<H", co, 0x3C)[0]
+    hdr = [struct.unpack_from("<IIQQQQIIQQ", co, shoff + 64 * i) for i in range(shnum)]
+    out = {}
+    for symtab in (h for h in hdr if h[1] == SHT_SYMTAB):
+        strtab = hdr[symtab[6]]
+        for k in range(symtab[5] // 24):
+            name_off, _info, _other, shndx, value, _size = struct.unpack_from("<IBBHQQ", co, symtab[4] + 24 * k)
+            start = strtab[4] + name_off
+            name = co[start:co.index(b"\0", start)].decode()
+            if name.endswith(".kd") and 0 < shndx < len(hdr):
+                sec = hdr[shndx]
+                rsrc1 = struct.unpack_from("<I", co, sec[4] + (value - sec[3]) + KD_RSRC1)[0]
+                out[name[:-3]] = ((rsrc1 & 0x3F) + 1) * 8
+    return out
+
+
 def _kernels_of_code_object(co: bytes):
     found = []
+    regs = _descriptor_registers(co)
     for _name, kind, off, size in _sections(co):
         if kind != SHT_NOTE:
             continue
@@ -53,7 +78,9 @@ def _kernels_of_code_object(co: bytes):
             desc = co[q:q + descsz]
             q += (descsz + 3) & ~3
             if ntype == NT_AMDGPU_METADATA and owner.startswith(b"AMDGPU"):
-                found += msgpack.unpackb(desc, raw=False)["amdhsa.kernels"]
+                for k in msgpack.unpackb(desc, raw=False)["amdhsa.kernels"]:
+                    k["allocated"] = regs[k[".name"]]
+                    found.append(k)
     return found
 
 
@@ -90,10 +117,11 @@ def kernels():
     assert len(names) == len(ks)
     table = {}
     for k, name in zip(ks, names):
-        regs = (k[".vgpr_count"] + 7) // 8 * 8
+        assert k["allocated"] >= k[".vgpr_count"], name  # .vgpr_count includes any AGPRs
         table[name.split("(")[0].removeprefix("void ")] = dict(
-            waves=min(8, 512 // regs), vgprs=k[".vgpr_count"], lds=k[".group_segment_fixed_size"],
-            scratch=k[".private_segment_fixed_size"], threads=k[".max_flat_workgroup_size"])
+            waves=min(8, 512 // k["allocated"]), vgprs=k[".vgpr_count"], allocated=k["allocated"],
+            lds=k[".group_segment_fixed_size"], scratch=k[".private_segment_fixed_size"],
+            threads=k[".max_flat_workgroup_size"])
     return table
 
 
@@ -158,6 +186,16 @@ def test_unmasked_noncausal_forms_hold_the_assumed_workgroups_per_cu(kernels, ti
         assert _wgs_per_cu(r) >= resident, (name, r)
 
 
+@pytest.mark.parametrize("ti", ["fa::BF16", "fa::F16"])
+def test_every_form_of_the_d128_default_tile_runs_three_waves_per_simd(kernels, ti):
+    """Split-KV and key-masked forms carry a three-wave bound; the others
+    stay below it by themselves."""
+    forms = _select(kernels, "fa::attn_fwd_kernel", a0="128", a1="32", a2="4", a3=ti)
+    assert len(forms) == 12  # {input dtype, fp32} output x causal x mask, and 4 split forms
+    for name, r in forms.items():
+        assert r["waves"] >= 3 and r["scratch"] == 0, (name, r)
+
+
 @pytest.mark.parametrize("d,resident", [(64, 2), (128, 1)])
 def test_fp32_input_tiles_hold_the_assumed_workgroups_per_cu(kernels, d, resident):
     forms = _select(kernels, "fa::attn_fwd_f32_kernel", a0=str(d), a1="64", a2="4")
@@ -174,11 +212,9 @@ def test_fused_d64_backward_fits_three_workgroups_per_cu(kernels):
 
 
 # Kernels allowed a few bytes of scratch (register spill), each below 16 bytes
-# per lane: the non-causal key-masked split forms of the d = 128 tile and the
-# largest 16-bit shape of the LDS-backed row softmax.
+# per lane: the bf16 forms of the largest 16-bit shape of the LDS-backed row
+# softmax.
 SPILL_ALLOWED = {
-    "fa::attn_fwd_kernel<128, 32, 4, fa::BF16, fa::BF16, false, true, true>",
-    "fa::attn_fwd_kernel<128, 32, 4, fa::F16, fa::F16, false, true, true>",
     "fa::softmax_resident_lds_kernel<fa::BF16, fa::BF16, 768, 14, 13>",
     "fa::softmax_resident_lds_kernel<fa::BF16, fa::F32, 768, 14, 13>",
 }
