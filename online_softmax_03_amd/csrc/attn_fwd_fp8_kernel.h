@@ -189,8 +189,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
     const bool wave_live = qw0 < N;
     const int qq = qw0 + col;
 
-    // K operand: row 32*kb + col, logical chunks 4m + 2*hh and +1.
+    // K operand: row 32*kb + col, logical chunks 4m + 2*hh and +1. The
+    // per-lane offsets within a tile are computed once, so both buffers and
+    // both key blocks read through the same registers with the rest in the
+    // instruction's constant offset.
     const int sw_col = swz<CH>(col);
+    u32 k_off[NDM][2];
+#pragma unroll
+    for (int m = 0; m < NDM; ++m)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) k_off[m][j] = (u32)(col * ROWB + (((4 * m + 2 * hh + j) ^ sw_col) << 4));
     // V^T by 8-bit transpose reads. Lane l of 16-lane group g (= l/16,
     // j = l%16) supplies, for output byte b' = j/2, the chunk of tile row
     // 16t + 8(b'/4) + 4*(g/2) + b'%4 (read t = 0..3) at d = 32db + 16(g%2) +
@@ -220,10 +228,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_fp8_kernel(ParamsFp8 p) {
         for (int m = 0; m < NDM; ++m) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const FA_LDS char* row = kt + (kb * 32 + col) * ROWB;
-                const int c0 = 4 * m + 2 * hh;
-                const u32x4 lo = *reinterpret_cast<const FA_LDS u32x4*>(row + ((c0 ^ sw_col) << 4));
-                const u32x4 hi = *reinterpret_cast<const FA_LDS u32x4*>(row + (((c0 + 1) ^ sw_col) << 4));
+                const FA_LDS char* blk = kt + kb * 32 * ROWB;
+                const u32x4 lo = *reinterpret_cast<const FA_LDS u32x4*>(blk + k_off[m][0]);
+                const u32x4 hi = *reinterpret_cast<const FA_LDS u32x4*>(blk + k_off[m][1]);
                 const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                 s[kb] = mfma_fp8(a, qop[m], s[kb]);
