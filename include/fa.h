@@ -121,9 +121,9 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /* fa_default_tile — the tile shape fa_fwd would use for these arguments:
  * for 16-bit inputs at d = 128, 256 x 64 when every workgroup has a long key
- * loop and the grid of 256-row tiles, G = B*H*ceil(N/256), still covers the
- * CUs (causal: N >= 8192, G >= 384 and, below N = 16384, G <= 1024;
- * non-causal: N >= 4096 and G >= 256), else the base tile. Writes *out and returns FA_OK, or returns a negative fa_status
+ * loop and the grid of 256-row tiles, G = B*H*ceil(N/256), holds about one to
+ * four workgroups per CU (causal: N >= 8192 and 384 <= G <= 1024;
+ * non-causal: N >= 4096 and 256 <= G <= 1024), else the base tile. Writes *out and returns FA_OK, or returns a negative fa_status
  * (FA_ERR_NULL, FA_ERR_SHAPE for B, H or N <= 0, FA_ERR_HEADDIM,
  * FA_ERR_DTYPE). Host only, no HIP call. */
 int fa_default_tile(int B, int H, int N, int d, fa_dtype_t in_dtype, fa_dtype_t out_dtype,

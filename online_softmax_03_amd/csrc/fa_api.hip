@@ -45,21 +45,21 @@ fa_tile default_tile(int d, int in_dtype) {
 
 // The tile fa_fwd takes when the caller names none. For 16-bit d = 128,
 // 256 x 64 (eight waves sharing every 64-key tile: half the LDS fills, waits
-// and barriers per MFMA of 128 x 32, at two waves per SIMD) is ahead once each
-// workgroup's key loop is long and its grid still covers the CUs. Same-process
-// A/B on two boxes: causal N = 32768 +2.3-3.5%, N = 16384 (8 heads) +3.5%,
-// N = 8192 with 16 heads +2.9-3.4% and 12 heads +17%, non-causal N = 8192
-// +5-10%, N = 4096 +2%. Behind with short loops (causal N <= 6144: -0.1 to
-// -2.4%, non-causal N = 2048: -0.7%) and with 256 or fewer causal workgroups
-// (-4.9 to -5.9%). Causal N = 8192 over 2048 workgroups (2 x 32 heads) is a
-// tie: +0.6-1.8% in same-process runs, -1.4% over three bench runs of each,
-// so the base tile keeps it.
+// and barriers per MFMA of 128 x 32, at two waves per SIMD) is ahead where
+// each workgroup's key loop is long and the grid of 256-row tiles, G, is
+// between about one and four workgroups per CU. Same-process A/B on three
+// boxes: causal N = 8192 at G = 384 +17%, G = 512 +2.5-3.4%, N = 16384 at
+// G = 512 +2.5-3.5%, N = 32768 at G = 1024 +0.7-3.5%; non-causal N = 8192 at
+// G = 256 +10-11%, 512 +7%, 1024 +2-5%, N = 4096 at G = 1024 +2-3%. Behind
+// or tied with short loops (causal N <= 6144: -0.1 to -2.4%, non-causal
+// N = 2048: -0.7%), with G <= 256 under a causal mask (-4.9 to -5.9%) and
+// with larger causal grids (N = 8192 at G = 2048: -0.6 to +1.8%, N = 16384
+// at G = 4096: -2.4%).
 fa_tile auto_tile(int B, int H, int N, int d, int in_dtype, int causal) {
     const fa_tile t = default_tile(d, in_dtype);
     if (in_dtype == FA_DTYPE_F32 || d != 128) return t;
-    const long long wide_grid = (long long)B * H * ((N + 255) / 256);
-    const bool wide = causal ? (N >= 8192 && wide_grid >= 384 && (N >= 16384 || wide_grid <= 1024))
-                             : (N >= 4096 && wide_grid >= 256);
+    const long long G = (long long)B * H * ((N + 255) / 256);
+    const bool wide = causal ? (N >= 8192 && G >= 384 && G <= 1024) : (N >= 4096 && G >= 256 && G <= 1024);
     return wide ? fa_tile{256, 64} : t;
 }
 

@@ -98,13 +98,14 @@ def test_default_tile_and_supported_tiles():
 @pytest.mark.parametrize("B,H,N,causal,tile", [
     # 16-bit d = 128: 256 x 64 for long key loops over a grid that covers the CUs
     (1, 8, 32768, 1, (256, 64)), (1, 12, 8192, 1, (256, 64)), (1, 16, 8192, 1, (256, 64)),
-    (1, 8, 16384, 1, (256, 64)), (2, 32, 16384, 1, (256, 64)), (4, 16, 4096, 0, (256, 64)),
-    (1, 8, 8192, 0, (256, 64)), (2, 32, 8192, 0, (256, 64)),
-    # short loops, 256 and fewer causal workgroups of 256 rows, or causal
-    # N = 8192 over more than 1024 of them: 128 x 32
-    (2, 32, 8192, 1, (128, 32)), (1, 8, 8192, 1, (128, 32)), (1, 4, 16384, 1, (128, 32)),
-    (2, 32, 6144, 1, (128, 32)), (4, 32, 4096, 1, (128, 32)), (8, 16, 2048, 0, (128, 32)),
-    (1, 4, 8192, 0, (128, 32)), (1, 1, 256, 0, (128, 32)),
+    (1, 8, 16384, 1, (256, 64)), (4, 16, 4096, 0, (256, 64)), (1, 8, 8192, 0, (256, 64)),
+    (2, 16, 8192, 0, (256, 64)),
+    # short loops, 256 and fewer causal workgroups of 256 rows, or more than
+    # 1024 of them: 128 x 32
+    (2, 32, 8192, 1, (128, 32)), (2, 32, 16384, 1, (128, 32)), (1, 8, 8192, 1, (128, 32)),
+    (1, 4, 16384, 1, (128, 32)), (2, 32, 6144, 1, (128, 32)), (4, 32, 4096, 1, (128, 32)),
+    (8, 16, 2048, 0, (128, 32)), (1, 4, 8192, 0, (128, 32)), (2, 32, 8192, 0, (128, 32)),
+    (1, 1, 256, 0, (128, 32)),
 ])
 def test_default_tile_follows_the_shape_rule(B, H, N, causal, tile):
     for dt in (BF16, F16):
