@@ -53,6 +53,10 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     prm.n_qtiles = (int)n_qtiles;
     prm.xcd_remap = fa::xcd_mode_for(B * H, grid);
     prm.head_group = fa::head_group_for(B * H, causal);
+    // Groups of four heads when every XCD holds a multiple of four (B*H a
+    // multiple of 32), as for the 16-bit forward: same process, causal
+    // N = 8192, 64 heads, G = 4 0.5591-0.5621 ms against G = 2 0.5701-0.5804.
+    if (causal && (long long)B * H % 32 == 0) prm.head_group = 4;
     prm.c = (float)((double)scale * descale_q * descale_k * 1.4426950408889634074);
     prm.descale_v = descale_v;
     void* args[] = {&prm};
