@@ -31,9 +31,11 @@ def attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: floa
 
     scale defaults to 1/sqrt(d). key_padding_mask: [B, N] bool/uint8 on the
     same device, True/nonzero = key valid. out_dtype defaults to q.dtype.
-    num_splits selects the split-KV path (`fa_fwd_splitkv`): an int >= 1, or
-    0 for the library's choice (`fa_splitkv_num_splits`); it uses the default
-    tile, so `tile` must then be None. `workspace` is an optional device
+    tile (block_r, block_c) forces a tile shape; None takes the library's
+    choice for the shape (`fa_default_tile`). num_splits selects the
+    split-KV path (`fa_fwd_splitkv`): an int >= 1, or 0 for the library's
+    choice (`fa_splitkv_num_splits`); it runs the base tile (128 x 32 at
+    d = 128, 256 x 64 at d = 64), so `tile` must then be None. `workspace` is an optional device
     buffer of at least `fa_splitkv_workspace_bytes` bytes (else one is
     allocated). Returns (o [B, H, N, d], lse [B, H, N] float32).
     """
@@ -69,7 +71,7 @@ def attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: floa
     stream = torch.cuda.current_stream(q.device).cuda_stream
     if num_splits is not None:
         if tile is not None:
-            raise ValueError("the split-KV path uses the default tile")
+            raise ValueError("the split-KV path runs the base tile; tile must be None")
         if num_splits == 0:
             num_splits = capi.fa_splitkv_num_splits(B, H, N, d, _DT[q.dtype], causal)
             if num_splits < 0:
