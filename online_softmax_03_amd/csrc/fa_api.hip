@@ -48,7 +48,7 @@ fa_tile default_tile(int d, int in_dtype) {
 // and barriers per MFMA of 128 x 32, at two waves per SIMD) is ahead where
 // each workgroup's key loop is long and the grid of 256-row tiles, G, is
 // between about one and four workgroups per CU. Same-process A/B on three
-// boxes: causal N = 8192 at G = 384 +17%, G = 512 +2.5-3.4%, N = 16384 at
+// MI355X cards: causal N = 8192 at G = 384 +17%, G = 512 +2.5-3.4%, N = 16384 at
 // G = 512 +2.5-3.5%, N = 32768 at G = 1024 +0.7-3.5%; non-causal N = 8192 at
 // G = 256 +10-11%, 512 +7%, 1024 +2-5%, N = 4096 at G = 1024 +2-3%. Behind
 // or tied with short loops (causal N <= 6144: -0.1 to -2.4%, non-causal
@@ -112,7 +112,7 @@ size_t splitkv_bytes(int B, int H, int N, int d, int S) {
 // there are CUs (B*H*ceil(N/block_r) <= 256), query tile qt gets parts in
 // proportion to its causal extent: at most u * block_r / block_c key tiles
 // each, num_splits (at most) for the last tile (parts_of, work_item.h). Every
-// query tile otherwise gets num_splits parts. Same-box comparisons on causal
+// query tile otherwise gets num_splits parts. Same-card comparisons on causal
 // d = 128, N = 8192 (TFLOP/s, equal parts against proportional parts, at the
 // best part count of each): 1 head 369 / 418, 2 heads 454 / 584, 4 heads 630
 // / 691; 8 heads 866 / 786 (512 query tiles: equal parts, 1024 workgroups of
@@ -297,7 +297,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
     // Causal 16-bit launches deal their query tiles in groups of four heads
     // when every XCD holds a multiple of four (B*H a multiple of 32): the
     // tail of the launch stays fuller than with pairs. Same process, causal
-    // d = 128, N = 8192, 64 heads, 128 x 32, two boxes: G = 4 0.9979-0.9984
+    // d = 128, N = 8192, 64 heads, 128 x 32, two cards: G = 4 0.9979-0.9984
     // ms against G = 2 1.0149-1.0237 (+1.7-2.6%), G = 8 1.0148, G = 1
     // 1.0604; for 256 x 64 G = 4 +0.4%. The K/V of four heads at once miss
     // the L2 more often (more fabric reads), which the launch absorbs.
@@ -343,7 +343,7 @@ int fa_splitkv_num_splits(int B, int H, int N, int d, fa_dtype_t in_dtype, int c
     if (split_plan(B, H, N, d, in_dtype, causal, 1).u > 0) {
         // Causal parts in proportion to the keys: the smallest count whose
         // workgroups reach 9/16 of the slots, at most 12, with at least four
-        // key tiles per part of the longest query tile. Same-box sweeps of
+        // key tiles per part of the longest query tile. Same-card sweeps of
         // 2 .. 24 on causal d = 128, N = 8192: the best counts were 6 - 12
         // for 1 head (219 - 374 workgroups), 6 for 2 heads (438), 3 for 4
         // heads (504); more parts than that lost 10 - 25%.
